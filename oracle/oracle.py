@@ -1,0 +1,210 @@
+"""CPU oracle for MoE dispatch/combine -- TEST INFRASTRUCTURE ONLY.
+
+Thin numpy/ctypes front end of ``epdc_oracle.c`` (plain C loops, single
+thread).  Only ``tests/``, the smoke check and the benchmark's CPU-baseline
+leg may import this module; the product path never does, and the HIP library
+shares no code with it.  See the C file's header for the passages of the MORI
+pages each step follows.
+
+The composition below follows the order the pages' dispatch implies: count
+the routing, scan it to expert and rank offsets, give every (token, k) pair a
+row, then copy (or quantize once per token and copy) the token's row and its
+weights/scales/indices rows to every row it owns.  Combine gathers the K rows
+of each token back and sums them with their weights in fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Dict, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "epdc_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+GCC_CMD = ["gcc", "-O2", "-std=c11", "-Wall", "-ffp-contract=off", "-shared", "-fPIC", _SRC]
+
+
+def build() -> str:
+    """Compile the oracle library in place (plain gcc, no fast-math)."""
+    tmp = _LIB_PATH + ".tmp"
+    cmd = GCC_CMD + ["-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    L = ctypes.c_long
+    lib.oracle_route.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
+    lib.oracle_route.restype = I
+    lib.oracle_scatter_rows.argtypes = [I, I, P, P, L, P]
+    lib.oracle_scatter_rows.restype = None
+    lib.oracle_quant_fp8.argtypes = [I, I, P, P, P]
+    lib.oracle_quant_fp8.restype = I
+    lib.oracle_quant_mxfp4.argtypes = [I, I, P, P, P]
+    lib.oracle_quant_mxfp4.restype = I
+    lib.oracle_combine.argtypes = [I, I, I, P, P, P, P, P]
+    lib.oracle_combine.restype = None
+    lib.oracle_e4m3_encode_array.argtypes = [L, P, P]
+    lib.oracle_e2m1_encode_array.argtypes = [L, P, P]
+    lib.oracle_f32_to_bf16_array.argtypes = [L, P, P]
+    _lib = lib
+    return lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---- scalar encoders (array forms) -----------------------------------------
+
+def e4m3_encode(v) -> np.ndarray:
+    v = _c(v, np.float32).ravel()
+    out = np.empty(v.size, np.uint8)
+    _load().oracle_e4m3_encode_array(v.size, _ptr(v), _ptr(out))
+    return out
+
+
+def e2m1_encode(v) -> np.ndarray:
+    v = _c(v, np.float64).ravel()
+    out = np.empty(v.size, np.uint8)
+    _load().oracle_e2m1_encode_array(v.size, _ptr(v), _ptr(out))
+    return out
+
+
+def f32_to_bf16(v) -> np.ndarray:
+    v = _c(v, np.float32).ravel()
+    out = np.empty(v.size, np.uint16)
+    _load().oracle_f32_to_bf16_array(v.size, _ptr(v), _ptr(out))
+    return out
+
+
+# ---- A1-A3 ------------------------------------------------------------------
+
+def route(indices: np.ndarray, num_experts: int, num_ranks: int) -> Dict[str, np.ndarray]:
+    """Histogram, exclusive scan and stable slots for int32 indices [T,K]."""
+    idx = _c(indices, np.int32)
+    T, K = idx.shape
+    E, R = int(num_experts), int(num_ranks)
+    n = T * K
+    cnt = np.zeros(E, np.int32)
+    expert_off = np.zeros(E + 1, np.int32)
+    rank_off = np.zeros(R + 1, np.int32)
+    recv_count = np.zeros(R, np.int32)
+    slot_of = np.zeros(n, np.int32)
+    src = np.full(n, -1, np.int32)
+    invalid = _load().oracle_route(T, K, E, R, _ptr(idx), _ptr(cnt), _ptr(expert_off),
+                                   _ptr(rank_off), _ptr(recv_count), _ptr(slot_of), _ptr(src))
+    if invalid < 0:
+        raise ValueError("oracle_route: bad arguments")
+    n_valid = n - invalid
+    return {"cnt": cnt, "expert_off": expert_off, "rank_off": rank_off,
+            "recv_count": recv_count, "slot_of": slot_of,
+            "src_token_pos": src[:n_valid].copy(), "invalid": invalid, "n_valid": n_valid}
+
+
+# ---- A4 / A4' -------------------------------------------------------------------
+
+def scatter_rows(src_rows: np.ndarray, slot_of: np.ndarray, topk: int, n_rows: int) -> np.ndarray:
+    """dst[slot_of[t*K+k]] = src_rows[t]; src_rows any dtype [T, ...]."""
+    src = np.ascontiguousarray(src_rows)
+    T = src.shape[0]
+    row_bytes = src.nbytes // T if T else src.itemsize
+    dst = np.zeros((n_rows,) + src.shape[1:], dtype=src.dtype)
+    so = _c(slot_of, np.int32)
+    _load().oracle_scatter_rows(T, int(topk), _ptr(so), _ptr(src), row_bytes, _ptr(dst))
+    return dst
+
+
+# ---- A5 / A6 ------------------------------------------------------------------
+
+def quant_fp8(x_bf16: np.ndarray):
+    """bf16 bits [T,H] -> (E4M3 codes uint8 [T,H], fp32 scales [T,H/128])."""
+    x = _c(x_bf16, np.uint16)
+    T, H = x.shape
+    q = np.empty((T, H), np.uint8)
+    s = np.empty((T, H // 128), np.float32)
+    if _load().oracle_quant_fp8(T, H, _ptr(x), _ptr(q), _ptr(s)) != 0:
+        raise ValueError("hidden must be a multiple of 128")
+    return q, s
+
+
+def quant_mxfp4(x_bf16: np.ndarray):
+    """bf16 bits [T,H] -> (packed E2M1 uint8 [T,H/2], E8M0 scales uint8 [T,H/32])."""
+    x = _c(x_bf16, np.uint16)
+    T, H = x.shape
+    q = np.empty((T, H // 2), np.uint8)
+    s = np.empty((T, H // 32), np.uint8)
+    if _load().oracle_quant_mxfp4(T, H, _ptr(x), _ptr(q), _ptr(s)) != 0:
+        raise ValueError("hidden must be a multiple of 32")
+    return q, s
+
+
+# ---- whole dispatch / combine --------------------------------------------------
+
+def dispatch(x: np.ndarray, weights: Optional[np.ndarray], indices: np.ndarray,
+             num_experts: int, num_ranks: int, quant: str = "none",
+             scales: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Reference dispatch.
+
+    ``x``: bf16 bits uint16 [T,H], or (quant "none" only) any byte rows [T,P]
+    to be carried unchanged.  ``scales``: optional per-token rows to carry
+    (quant "none" only).  Returns the received rows for the n_valid valid
+    pairs, in slot order: ``out``, ``out_weights``, ``out_scales``,
+    ``out_indices``, plus the routing (``recv_count``, ``expert_off``,
+    ``rank_off``, ``slot_of``, ``src_token_pos``).
+    """
+    idx = _c(indices, np.int32)
+    T, K = idx.shape
+    r = route(idx, num_experts, num_ranks)
+    n = r["n_valid"]
+    so = r["slot_of"]
+    if quant == "none":
+        payload, sc = x, scales
+    elif quant == "fp8_e4m3_b128":
+        if scales is not None:
+            raise ValueError("scales are produced by quantization")
+        payload, sc = quant_fp8(x)
+    elif quant == "mxfp4_b32":
+        if scales is not None:
+            raise ValueError("scales are produced by quantization")
+        payload, sc = quant_mxfp4(x)
+    else:
+        raise ValueError(quant)
+    out = dict(r)
+    out["out"] = scatter_rows(payload, so, K, n)
+    out["out_indices"] = scatter_rows(idx, so, K, n)
+    out["out_weights"] = None if weights is None else scatter_rows(_c(weights, np.float32), so, K, n)
+    out["out_scales"] = None if sc is None else scatter_rows(sc, so, K, n)
+    return out
+
+
+def combine(inp: np.ndarray, weights: Optional[np.ndarray], slot_of: np.ndarray,
+            tokens: int, topk: int):
+    """Reference combine: bf16 bits [N,H] (received layout) -> (bf16 bits [T,H], fp32 [T,K])."""
+    x = _c(inp, np.uint16)
+    H = x.shape[1]
+    so = _c(slot_of, np.int32)
+    w = None if weights is None else _c(weights, np.float32)
+    out = np.empty((tokens, H), np.uint16)
+    out_w = np.empty((tokens, topk), np.float32)
+    _load().oracle_combine(int(tokens), H, int(topk), _ptr(so), _ptr(x), _ptr(w),
+                           _ptr(out), _ptr(out_w))
+    return out, out_w
