@@ -1,0 +1,196 @@
+"""ctypes binding of libepdc.so (include/epdc.h), one Python function per C
+entry point with the same name.  Arguments are plain integers (device
+addresses, sizes, a hipStream_t as an integer); this layer only marshals them
+and turns a non-SUCCESS status into an exception.  It has no fallback: if the
+HIP library is not built it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import List, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB_PATH = os.path.join(PKG, "libepdc.so")
+HEADER = os.path.join(ROOT, "include", "epdc.h")
+
+EPDC_SUCCESS = 0
+EPDC_ERR_INVALID_ARGS = -1
+EPDC_ERR_BAD_STATE = -2
+EPDC_ERR_GPU_OP = -3
+EPDC_ERR_UNSUPPORTED = -4
+EPDC_ERR_NOT_FOUND = -5
+STATUS_NAMES = {0: "SUCCESS", -1: "ERR_INVALID_ARGS", -2: "ERR_BAD_STATE", -3: "ERR_GPU_OP",
+                -4: "ERR_UNSUPPORTED", -5: "ERR_NOT_FOUND"}
+
+EPDC_IN_BF16 = 0
+EPDC_IN_RAW = 1
+EPDC_QUANT_NONE = 0
+EPDC_QUANT_FP8_E4M3_B128 = 1
+EPDC_QUANT_MXFP4_B32 = 2
+
+EPDC_KERNEL_ROUTE = 0
+EPDC_KERNEL_SCATTER = 1
+EPDC_KERNEL_SCATTER_FP8 = 2
+EPDC_KERNEL_SCATTER_MXFP4 = 3
+EPDC_KERNEL_COMBINE = 4
+EPDC_NUM_KERNELS = 5
+
+
+class epdc_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "max_tokens", "hidden", "topk", "num_experts", "num_ranks",
+        "input_kind", "quant", "raw_row_bytes", "scale_row_bytes")]
+
+
+class EpdcError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+P = ctypes.c_void_p
+I32 = ctypes.c_int32
+PI32 = ctypes.POINTER(ctypes.c_int32)
+SZ = ctypes.c_size_t
+PCFG = ctypes.POINTER(epdc_config)
+
+_SIGNATURES = {
+    "epdc_workspace_bytes": (I32, [PCFG, ctypes.POINTER(SZ)]),
+    "epdc_row_bytes": (I32, [PCFG, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
+    "epdc_create": (I32, [PCFG, P, SZ, ctypes.POINTER(P)]),
+    "epdc_destroy": (I32, [P]),
+    "epdc_dispatch": (I32, [P, P, I32, P, P, P, P, P, P, P, P, P]),
+    "epdc_combine": (I32, [P, P, P, P, P, P, P]),
+    "epdc_get_dispatch_src_token_pos": (I32, [P, ctypes.POINTER(P), PI32]),
+    "epdc_get_routing": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P)]),
+    "epdc_get_device_error": (I32, [P, P, PI32]),
+    "epdc_reset": (I32, [P]),
+    "epdc_last_error": (ctypes.c_char_p, []),
+    "epdc_kernel_name": (ctypes.c_char_p, [I32]),
+    "epdc_profile_begin": (I32, [P, I32]),
+    "epdc_profile_end": (I32, [P, ctypes.POINTER(ctypes.c_float), PI32]),
+}
+
+
+def lib():
+    """Load libepdc.so; raises if it has not been built (no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; build it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python -m combine_routing_histogram_amd.build`")
+    l = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        f = getattr(l, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = l
+    return l
+
+
+def header_entry_points() -> List[str]:
+    """Names of the functions include/epdc.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\**\s*(epdc_[a-z_]+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def _check(status: int) -> None:
+    if status != EPDC_SUCCESS:
+        raise EpdcError(status, lib().epdc_last_error().decode())
+
+
+def make_config(max_tokens: int, hidden: int, topk: int, num_experts: int, num_ranks: int,
+                input_kind: int = EPDC_IN_BF16, quant: int = EPDC_QUANT_NONE,
+                raw_row_bytes: int = 0, scale_row_bytes: int = 0) -> epdc_config:
+    return epdc_config(max_tokens, hidden, topk, num_experts, num_ranks, input_kind, quant,
+                       raw_row_bytes, scale_row_bytes)
+
+
+# ---- one wrapper per entry point --------------------------------------------------
+
+def epdc_workspace_bytes(cfg: epdc_config) -> int:
+    n = SZ(0)
+    _check(lib().epdc_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def epdc_row_bytes(cfg: epdc_config) -> Tuple[int, int]:
+    a, b = SZ(0), SZ(0)
+    _check(lib().epdc_row_bytes(ctypes.byref(cfg), ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def epdc_create(cfg: epdc_config, workspace: int, workspace_bytes: int) -> int:
+    op = P(None)
+    _check(lib().epdc_create(ctypes.byref(cfg), workspace, workspace_bytes, ctypes.byref(op)))
+    return op.value
+
+
+def epdc_destroy(op: int) -> None:
+    _check(lib().epdc_destroy(op))
+
+
+def epdc_dispatch(op: int, stream: int, num_tokens: int, input: int, weights: int,
+                  scales: int, indices: int, out: int, out_weights: int, out_scales: int,
+                  out_indices: int, recv_count: int) -> None:
+    _check(lib().epdc_dispatch(op, stream or None, num_tokens, input or None, weights or None,
+                               scales or None, indices or None, out or None,
+                               out_weights or None, out_scales or None, out_indices or None,
+                               recv_count or None))
+
+
+def epdc_combine(op: int, stream: int, input: int, weights: int, indices: int, output: int,
+                 out_weights: int) -> None:
+    _check(lib().epdc_combine(op, stream or None, input or None, weights or None,
+                              indices or None, output or None, out_weights or None))
+
+
+def epdc_get_dispatch_src_token_pos(op: int) -> Tuple[int, int]:
+    ptr, n = P(None), I32(0)
+    _check(lib().epdc_get_dispatch_src_token_pos(op, ctypes.byref(ptr), ctypes.byref(n)))
+    return ptr.value, n.value
+
+
+def epdc_get_routing(op: int) -> Tuple[int, int, int]:
+    a, b, c = P(None), P(None), P(None)
+    _check(lib().epdc_get_routing(op, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def epdc_get_device_error(op: int, stream: int) -> int:
+    f = I32(0)
+    _check(lib().epdc_get_device_error(op, stream or None, ctypes.byref(f)))
+    return f.value
+
+
+def epdc_reset(op: int) -> None:
+    _check(lib().epdc_reset(op))
+
+
+def epdc_last_error() -> str:
+    return lib().epdc_last_error().decode()
+
+
+def epdc_kernel_name(kernel_id: int):
+    r = lib().epdc_kernel_name(kernel_id)
+    return None if r is None else r.decode()
+
+
+def epdc_profile_begin(op: int, max_launches: int) -> None:
+    _check(lib().epdc_profile_begin(op, max_launches))
+
+
+def epdc_profile_end(op: int) -> Tuple[List[float], List[int]]:
+    ms = (ctypes.c_float * EPDC_NUM_KERNELS)()
+    n = (ctypes.c_int32 * EPDC_NUM_KERNELS)()
+    _check(lib().epdc_profile_end(op, ms, n))
+    return list(ms), list(n)

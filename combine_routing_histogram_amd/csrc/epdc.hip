@@ -1,0 +1,559 @@
+// epdc.hip -- host side of the C ABI declared in include/epdc.h: argument
+// checks, workspace layout, kernel selection and launch, per-kernel event
+// timing.  Every step of dispatch and combine runs in the kernels of
+// epdc_kernels.hpp; the host enqueues them on the caller's stream and never
+// waits, except in epdc_create (control words cleared once),
+// epdc_get_device_error and epdc_profile_end.
+#include "epdc.h"
+#include "epdc_kernels.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace epdc;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+epdc_status fail(epdc_status s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+epdc_status ok()
+{
+    g_last_error.clear();
+    return EPDC_SUCCESS;
+}
+
+constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Device workspace: control words, routing tables and the per-pair arrays.
+struct Layout {
+    size_t ctrl, tile_table, rank_in_tile, expert_off, rank_off, slot_of, src_pos, total;
+    int64_t n_cap;
+    int64_t tiles_max;
+};
+
+epdc_status check_config(const epdc_config *c)
+{
+    if (!c)
+        return fail(EPDC_ERR_INVALID_ARGS, "config is NULL");
+    if (c->max_tokens < 0)
+        return fail(EPDC_ERR_INVALID_ARGS, "max_tokens must be >= 0");
+    if (c->hidden <= 0 || c->hidden % 8 != 0)
+        return fail(EPDC_ERR_INVALID_ARGS, "hidden must be a positive multiple of 8");
+    if (c->topk < 1 || c->topk > kMaxTopk)
+        return fail(EPDC_ERR_INVALID_ARGS, "topk must be in [1, %d]", kMaxTopk);
+    if (c->num_experts < 1 || c->num_experts > kMaxExperts)
+        return fail(EPDC_ERR_INVALID_ARGS, "num_experts must be in [1, %d]", kMaxExperts);
+    if (c->num_ranks < 1 || c->num_experts % c->num_ranks != 0)
+        return fail(EPDC_ERR_INVALID_ARGS, "num_ranks must divide num_experts");
+    if ((int64_t)c->max_tokens * c->topk > (int64_t)(1 << 30))
+        return fail(EPDC_ERR_INVALID_ARGS, "max_tokens*topk must be <= 2^30");
+    if (c->input_kind != EPDC_IN_BF16 && c->input_kind != EPDC_IN_RAW)
+        return fail(EPDC_ERR_INVALID_ARGS, "unknown input_kind %d", c->input_kind);
+    if (c->scale_row_bytes < 0 || c->scale_row_bytes % 4 != 0)
+        return fail(EPDC_ERR_INVALID_ARGS, "scale_row_bytes must be a non-negative multiple of 4");
+    switch (c->quant) {
+    case EPDC_QUANT_NONE:
+        break;
+    case EPDC_QUANT_FP8_E4M3_B128:
+        if (c->hidden % 128 != 0)
+            return fail(EPDC_ERR_INVALID_ARGS, "FP8 block-128 quantization needs hidden %% 128 == 0");
+        break;
+    case EPDC_QUANT_MXFP4_B32:
+        if (c->hidden % 32 != 0)
+            return fail(EPDC_ERR_INVALID_ARGS, "MXFP4 quantization needs hidden %% 32 == 0");
+        break;
+    default:
+        return fail(EPDC_ERR_INVALID_ARGS, "unknown quant %d", c->quant);
+    }
+    if (c->quant != EPDC_QUANT_NONE) {
+        if (c->input_kind != EPDC_IN_BF16)
+            return fail(EPDC_ERR_INVALID_ARGS, "quantization needs bf16 input");
+        if (c->scale_row_bytes != 0)
+            return fail(EPDC_ERR_INVALID_ARGS, "scale_row_bytes must be 0 when dispatch quantizes");
+    }
+    if (c->input_kind == EPDC_IN_RAW && (c->raw_row_bytes <= 0 || c->raw_row_bytes % 16 != 0))
+        return fail(EPDC_ERR_INVALID_ARGS, "raw_row_bytes must be a positive multiple of 16");
+    return EPDC_SUCCESS;
+}
+
+Layout layout_for(const epdc_config &c)
+{
+    Layout l{};
+    l.n_cap = (int64_t)c.max_tokens * c.topk;
+    l.tiles_max = l.n_cap > 0 ? (l.n_cap + kRouteTile - 1) / kRouteTile : 1;
+    size_t off = 0;
+    l.ctrl = off;
+    off += align256(sizeof(uint32_t) * kCtrlWords);
+    l.tile_table = off;
+    off += align256(sizeof(int32_t) * (size_t)l.tiles_max * c.num_experts);
+    l.rank_in_tile = off;
+    off += align256(sizeof(int32_t) * (size_t)l.n_cap);
+    l.expert_off = off;
+    off += align256(sizeof(int32_t) * (size_t)(c.num_experts + 1));
+    l.rank_off = off;
+    off += align256(sizeof(int32_t) * (size_t)(c.num_ranks + 1));
+    l.slot_of = off;
+    off += align256(sizeof(int32_t) * (size_t)l.n_cap);
+    l.src_pos = off;
+    off += align256(sizeof(int32_t) * (size_t)l.n_cap);
+    l.total = off;
+    return l;
+}
+
+void row_bytes_for(const epdc_config &c, size_t *payload, size_t *scales)
+{
+    switch (c.quant) {
+    case EPDC_QUANT_FP8_E4M3_B128:
+        *payload = (size_t)c.hidden;
+        *scales = sizeof(float) * (size_t)(c.hidden / 128);
+        return;
+    case EPDC_QUANT_MXFP4_B32:
+        *payload = (size_t)c.hidden / 2;
+        *scales = (size_t)c.hidden / 32;
+        return;
+    default:
+        *payload = c.input_kind == EPDC_IN_RAW ? (size_t)c.raw_row_bytes : 2 * (size_t)c.hidden;
+        *scales = (size_t)c.scale_row_bytes;
+        return;
+    }
+}
+
+const char *const kKernelNames[EPDC_NUM_KERNELS] = {
+    "k_route", "k_scatter_copy", "k_scatter_fp8", "k_scatter_mxfp4", "k_combine"};
+
+}  // namespace
+
+struct epdc_op {
+    epdc_config cfg;
+    int device;
+    uint8_t *ws;
+    Layout lay;
+    int key_bits;
+    bool routed;
+    int32_t last_tokens;
+    // per-kernel timing
+    bool profiling;
+    int ev_cap, ev_used;
+    std::vector<hipEvent_t> ev;  // 2 per launch
+    std::vector<int> ev_kernel;
+
+    uint32_t *ctrl() const { return reinterpret_cast<uint32_t *>(ws + lay.ctrl); }
+    int32_t *i32(size_t off) const { return reinterpret_cast<int32_t *>(ws + off); }
+};
+
+namespace {
+
+// Launch `f` on `st`, bracketed by timing events when profiling.
+template <typename F>
+epdc_status launch(epdc_op *op, hipStream_t st, int kernel_id, F &&f)
+{
+    const bool prof = op->profiling && op->ev_used < op->ev_cap;
+    hipError_t ev_err = hipSuccess;
+    if (prof)
+        ev_err = hipEventRecord(op->ev[2 * op->ev_used], st);
+    f();
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return fail(EPDC_ERR_GPU_OP, "%s launch failed: %s", kKernelNames[kernel_id],
+                    hipGetErrorString(err));
+    if (prof) {
+        if (ev_err == hipSuccess)
+            ev_err = hipEventRecord(op->ev[2 * op->ev_used + 1], st);
+        if (ev_err != hipSuccess)
+            return fail(EPDC_ERR_GPU_OP, "hipEventRecord: %s", hipGetErrorString(ev_err));
+        op->ev_kernel[op->ev_used] = kernel_id;
+        ++op->ev_used;
+    }
+    return EPDC_SUCCESS;
+}
+
+// One wave per token; bigger blocks once there are enough tokens to fill the
+// chip with them.
+int waves_per_block(int tokens) { return tokens >= 2048 ? 4 : 1; }
+
+template <int KT, int CH>
+void launch_combine(int grid, int block, hipStream_t st, const CombineArgs &a)
+{
+    k_combine<KT, CH><<<grid, block, 0, st>>>(a);
+}
+
+}  // namespace
+
+extern "C" {
+
+epdc_status epdc_workspace_bytes(const epdc_config *cfg, size_t *bytes)
+{
+    epdc_status s = check_config(cfg);
+    if (s != EPDC_SUCCESS)
+        return s;
+    if (!bytes)
+        return fail(EPDC_ERR_INVALID_ARGS, "bytes is NULL");
+    *bytes = layout_for(*cfg).total;
+    return ok();
+}
+
+epdc_status epdc_row_bytes(const epdc_config *cfg, size_t *payload_bytes, size_t *scale_bytes)
+{
+    epdc_status s = check_config(cfg);
+    if (s != EPDC_SUCCESS)
+        return s;
+    if (!payload_bytes || !scale_bytes)
+        return fail(EPDC_ERR_INVALID_ARGS, "output pointer is NULL");
+    row_bytes_for(*cfg, payload_bytes, scale_bytes);
+    return ok();
+}
+
+epdc_status epdc_create(const epdc_config *cfg, void *workspace, size_t workspace_bytes,
+                        epdc_op **op)
+{
+    epdc_status s = check_config(cfg);
+    if (s != EPDC_SUCCESS)
+        return s;
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    *op = nullptr;
+    const Layout lay = layout_for(*cfg);
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0)
+        return fail(EPDC_ERR_INVALID_ARGS, "workspace must be a 256-byte aligned device pointer");
+    if (workspace_bytes < lay.total)
+        return fail(EPDC_ERR_INVALID_ARGS, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                    lay.total);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(EPDC_ERR_GPU_OP, "hipGetDevice: %s", hipGetErrorString(e));
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+        return fail(EPDC_ERR_GPU_OP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(EPDC_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950",
+                    dev, prop.gcnArchName);
+    e = hipMemset(static_cast<uint8_t *>(workspace) + lay.ctrl, 0, sizeof(uint32_t) * kCtrlWords);
+    if (e == hipSuccess)
+        e = hipDeviceSynchronize();
+    if (e != hipSuccess)
+        return fail(EPDC_ERR_GPU_OP, "clearing control words: %s", hipGetErrorString(e));
+
+    epdc_op *o = new epdc_op();
+    o->cfg = *cfg;
+    o->device = dev;
+    o->ws = static_cast<uint8_t *>(workspace);
+    o->lay = lay;
+    int bits = 0;
+    while ((1 << bits) < cfg->num_experts)
+        ++bits;
+    o->key_bits = bits;
+    o->routed = false;
+    o->last_tokens = 0;
+    o->profiling = false;
+    o->ev_cap = o->ev_used = 0;
+    *op = o;
+    return ok();
+}
+
+epdc_status epdc_destroy(epdc_op *op)
+{
+    if (!op)
+        return ok();
+    for (hipEvent_t ev : op->ev)
+        (void)hipEventDestroy(ev);
+    delete op;
+    return ok();
+}
+
+epdc_status epdc_dispatch(epdc_op *op, void *stream, int32_t num_tokens, const void *input,
+                          const float *weights, const void *scales, const int32_t *indices,
+                          void *out, float *out_weights, void *out_scales, int32_t *out_indices,
+                          int32_t *recv_count)
+{
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    const epdc_config &c = op->cfg;
+    if (num_tokens < 0 || num_tokens > c.max_tokens)
+        return fail(EPDC_ERR_INVALID_ARGS, "num_tokens %d outside [0, %d]", num_tokens,
+                    c.max_tokens);
+    if (!out || !recv_count)
+        return fail(EPDC_ERR_INVALID_ARGS, "out and recv_count are required");
+    const bool quant = c.quant != EPDC_QUANT_NONE;
+    if (num_tokens > 0) {  // with no tokens no row is read or written
+        if (!input || !indices)
+            return fail(EPDC_ERR_INVALID_ARGS, "input and indices are required");
+        if ((weights == nullptr) != (out_weights == nullptr))
+            return fail(EPDC_ERR_INVALID_ARGS,
+                        "weights and out_weights must both be given or both NULL");
+        if (quant) {
+            if (scales)
+                return fail(EPDC_ERR_INVALID_ARGS, "scales must be NULL: dispatch produces them");
+            if (!out_scales)
+                return fail(EPDC_ERR_INVALID_ARGS,
+                            "out_scales is required when dispatch quantizes");
+        } else if (scales) {
+            if (c.scale_row_bytes == 0)
+                return fail(EPDC_ERR_INVALID_ARGS, "scales given but scale_row_bytes is 0");
+            if (!out_scales)
+                return fail(EPDC_ERR_INVALID_ARGS, "out_scales is required to carry scales");
+        }
+    }
+
+    if (!aligned(input, 16) || !aligned(out, 16) || !aligned(weights, 4) ||
+        !aligned(indices, 4) || !aligned(scales, 4) || !aligned(out_weights, 4) ||
+        !aligned(out_scales, 4) || !aligned(out_indices, 4) || !aligned(recv_count, 4))
+        return fail(EPDC_ERR_INVALID_ARGS,
+                    "input/out must be 16-byte aligned, the other arrays 4-byte aligned");
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int n_pairs = num_tokens * c.topk;
+    const int tiles = n_pairs > 0 ? (n_pairs + kRouteTile - 1) / kRouteTile : 1;
+
+    RouteArgs ra;
+    ra.indices = indices;
+    ra.n_pairs = n_pairs;
+    ra.num_experts = c.num_experts;
+    ra.num_ranks = c.num_ranks;
+    ra.key_bits = op->key_bits;
+    ra.tile_table = op->i32(op->lay.tile_table);
+    ra.rank_in_tile = op->i32(op->lay.rank_in_tile);
+    ra.expert_off = op->i32(op->lay.expert_off);
+    ra.rank_off = op->i32(op->lay.rank_off);
+    ra.recv_count = recv_count;
+    ra.ctrl = op->ctrl();
+    const size_t lds = sizeof(int32_t) * (size_t)route_lds_ints(c.num_experts);
+    epdc_status s = launch(op, st, EPDC_KERNEL_ROUTE, [&] {
+        k_route<<<tiles, kRouteThreads, lds, st>>>(ra);
+    });
+    if (s != EPDC_SUCCESS)
+        return s;
+
+    op->routed = true;
+    op->last_tokens = num_tokens;
+    if (num_tokens == 0)
+        return ok();
+
+    ScatterArgs sa;
+    sa.num_tokens = num_tokens;
+    sa.n_pairs = n_pairs;
+    sa.topk = c.topk;
+    sa.num_experts = c.num_experts;
+    sa.hidden = c.hidden;
+    sa.indices = indices;
+    sa.tile_table = ra.tile_table;
+    sa.rank_in_tile = ra.rank_in_tile;
+    sa.slot_of = op->i32(op->lay.slot_of);
+    sa.src_pos = op->i32(op->lay.src_pos);
+    sa.input = static_cast<const uint8_t *>(input);
+    sa.in_row_vecs = c.input_kind == EPDC_IN_RAW ? c.raw_row_bytes / 16 : c.hidden / 8;
+    sa.out = static_cast<uint8_t *>(out);
+    sa.weights = weights;
+    sa.out_weights = out_weights;
+    sa.out_indices = out_indices;
+    sa.scales = quant ? nullptr : static_cast<const uint8_t *>(scales);
+    sa.out_scales = static_cast<uint8_t *>(out_scales);
+    sa.scale_words = c.scale_row_bytes / 4;
+    sa.ctrl = op->ctrl();
+
+    const int wpb = waves_per_block(num_tokens);
+    const int grid = (num_tokens + wpb - 1) / wpb;
+    const int block = wpb * kWave;
+    switch (c.quant) {
+    case EPDC_QUANT_FP8_E4M3_B128:
+        s = launch(op, st, EPDC_KERNEL_SCATTER_FP8,
+                   [&] { k_scatter_fp8<4><<<grid, block, 0, st>>>(sa); });
+        break;
+    case EPDC_QUANT_MXFP4_B32:
+        s = launch(op, st, EPDC_KERNEL_SCATTER_MXFP4,
+                   [&] { k_scatter_mxfp4<4><<<grid, block, 0, st>>>(sa); });
+        break;
+    default:
+        s = launch(op, st, EPDC_KERNEL_SCATTER,
+                   [&] { k_scatter_copy<8><<<grid, block, 0, st>>>(sa); });
+        break;
+    }
+    if (s != EPDC_SUCCESS)
+        return s;
+    return ok();
+}
+
+epdc_status epdc_combine(epdc_op *op, void *stream, const void *input, const float *weights,
+                         const int32_t *indices, void *output, float *out_weights)
+{
+    (void)indices;  // the op keeps the routing of the last dispatch
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    if (!op->routed)
+        return fail(EPDC_ERR_BAD_STATE, "combine needs a dispatch first (none since create/reset)");
+    const epdc_config &c = op->cfg;
+    const int T = op->last_tokens;
+    if (T == 0)
+        return ok();
+    if (!input || !output)
+        return fail(EPDC_ERR_INVALID_ARGS, "input and output are required");
+    if (!aligned(input, 16) || !aligned(output, 16) || !aligned(weights, 4) ||
+        !aligned(out_weights, 4))
+        return fail(EPDC_ERR_INVALID_ARGS,
+                    "input/output must be 16-byte aligned, weights 4-byte aligned");
+
+    CombineArgs ca;
+    ca.num_tokens = T;
+    ca.topk = c.topk;
+    ca.row_vecs = c.hidden / 8;
+    ca.slot_of = op->i32(op->lay.slot_of);
+    ca.input = static_cast<const uint8_t *>(input);
+    ca.weights = weights;
+    ca.output = static_cast<uint8_t *>(output);
+    ca.out_weights = out_weights;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int wpb = waves_per_block(T);
+    const int grid = (T + wpb - 1) / wpb;
+    const int block = wpb * kWave;
+    epdc_status s = launch(op, st, EPDC_KERNEL_COMBINE, [&] {
+        switch (c.topk) {
+        case 1: launch_combine<1, 4>(grid, block, st, ca); break;
+        case 2: launch_combine<2, 4>(grid, block, st, ca); break;
+        case 4: launch_combine<4, 2>(grid, block, st, ca); break;
+        case 6: launch_combine<6, 2>(grid, block, st, ca); break;
+        case 8: launch_combine<8, 2>(grid, block, st, ca); break;
+        default: launch_combine<kMaxTopk, 1>(grid, block, st, ca); break;
+        }
+    });
+    if (s != EPDC_SUCCESS)
+        return s;
+    return ok();
+}
+
+epdc_status epdc_get_dispatch_src_token_pos(epdc_op *op, const int32_t **dev_ptr, int32_t *count)
+{
+    if (!op || !dev_ptr || !count)
+        return fail(EPDC_ERR_INVALID_ARGS, "NULL argument");
+    if (!op->routed)
+        return fail(EPDC_ERR_BAD_STATE, "no dispatch recorded");
+    *dev_ptr = op->i32(op->lay.src_pos);
+    *count = op->last_tokens * op->cfg.topk;
+    return ok();
+}
+
+epdc_status epdc_get_routing(epdc_op *op, const int32_t **expert_off, const int32_t **rank_off,
+                             const int32_t **slot_of)
+{
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    if (!op->routed)
+        return fail(EPDC_ERR_BAD_STATE, "no dispatch recorded");
+    if (expert_off)
+        *expert_off = op->i32(op->lay.expert_off);
+    if (rank_off)
+        *rank_off = op->i32(op->lay.rank_off);
+    if (slot_of)
+        *slot_of = op->i32(op->lay.slot_of);
+    return ok();
+}
+
+epdc_status epdc_get_device_error(epdc_op *op, void *stream, int32_t *flag)
+{
+    if (!op || !flag)
+        return fail(EPDC_ERR_INVALID_ARGS, "NULL argument");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint32_t v = 0;
+    hipError_t e = hipStreamSynchronize(st);
+    if (e == hipSuccess)
+        e = hipMemcpy(&v, op->ctrl() + kCtrlError, sizeof v, hipMemcpyDeviceToHost);
+    if (e == hipSuccess)
+        e = hipMemset(op->ctrl() + kCtrlError, 0, sizeof v);
+    if (e == hipSuccess)
+        e = hipDeviceSynchronize();
+    if (e != hipSuccess)
+        return fail(EPDC_ERR_GPU_OP, "reading the device error flag: %s", hipGetErrorString(e));
+    *flag = (int32_t)v;
+    return ok();
+}
+
+epdc_status epdc_reset(epdc_op *op)
+{
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    op->routed = false;
+    op->last_tokens = 0;
+    return ok();
+}
+
+const char *epdc_last_error(void) { return g_last_error.c_str(); }
+
+const char *epdc_kernel_name(int32_t kernel_id)
+{
+    if (kernel_id < 0 || kernel_id >= EPDC_NUM_KERNELS)
+        return nullptr;
+    return kKernelNames[kernel_id];
+}
+
+epdc_status epdc_profile_begin(epdc_op *op, int32_t max_launches)
+{
+    if (!op || max_launches <= 0)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL or max_launches <= 0");
+    for (hipEvent_t ev : op->ev)
+        (void)hipEventDestroy(ev);
+    op->ev.assign(2 * (size_t)max_launches, nullptr);
+    op->ev_kernel.assign((size_t)max_launches, -1);
+    for (auto &ev : op->ev) {
+        hipError_t e = hipEventCreate(&ev);
+        if (e != hipSuccess) {
+            op->profiling = false;
+            return fail(EPDC_ERR_GPU_OP, "hipEventCreate: %s", hipGetErrorString(e));
+        }
+    }
+    op->ev_cap = max_launches;
+    op->ev_used = 0;
+    op->profiling = true;
+    return ok();
+}
+
+epdc_status epdc_profile_end(epdc_op *op, float *ms, int32_t *launches)
+{
+    if (!op || !ms || !launches)
+        return fail(EPDC_ERR_INVALID_ARGS, "NULL argument");
+    if (!op->profiling)
+        return fail(EPDC_ERR_BAD_STATE, "profiling was not started");
+    for (int k = 0; k < EPDC_NUM_KERNELS; ++k) {
+        ms[k] = 0.0f;
+        launches[k] = 0;
+    }
+    epdc_status st = EPDC_SUCCESS;
+    if (op->ev_used > 0) {
+        hipError_t e = hipEventSynchronize(op->ev[2 * op->ev_used - 1]);
+        for (int i = 0; e == hipSuccess && i < op->ev_used; ++i) {
+            float t = 0.0f;
+            e = hipEventElapsedTime(&t, op->ev[2 * i], op->ev[2 * i + 1]);
+            ms[op->ev_kernel[i]] += t;
+            launches[op->ev_kernel[i]] += 1;
+        }
+        if (e != hipSuccess)
+            st = fail(EPDC_ERR_GPU_OP, "reading timing events: %s", hipGetErrorString(e));
+    }
+    for (hipEvent_t ev : op->ev)
+        (void)hipEventDestroy(ev);
+    op->ev.clear();
+    op->ev_kernel.clear();
+    op->ev_cap = op->ev_used = 0;
+    op->profiling = false;
+    return st == EPDC_SUCCESS ? ok() : st;
+}
+
+}  // extern "C"

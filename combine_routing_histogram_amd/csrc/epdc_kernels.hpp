@@ -1,0 +1,607 @@
+// epdc_kernels.hpp -- gfx950 (CDNA4) kernels of the MoE dispatch/combine hot
+// path: routing histogram + scan + stable in-tile ranks, slot assignment fused
+// with the payload scatter (bf16/raw copy, OCP E4M3 or MXFP4 quantization on
+// the fly), and the gather combine.
+//
+// What is computed follows MORI's EpDispatchCombineOp methods (MORI
+// "Communication APIs" page, MORI-EP section, methods table) on one GPU with
+// the destination ranks as contiguous segments of one receive buffer; the
+// count is produced by the dispatch kernels themselves (same page, "AsyncLL v2
+// SDMA overlap" section).  Gather combine in BF16 with FP32 accumulation and
+// the FP8/FP4 formats are the ones the "Choosing an EP API and backend" page
+// lists for gfx950 ("EP paths" table and EPv2 restrictions list).
+//
+// Work is data movement, so nothing here uses MFMA: one wavefront (64 lanes)
+// owns one token row, rows move as 16-byte vectors per lane, and the routing
+// uses wave ballots instead of atomics so the slot order is deterministic.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace epdc {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kRouteThreads = 1024;                 // one pair per thread
+constexpr int kRouteWaves = kRouteThreads / kWave;  // 16
+constexpr int kRouteTile = kRouteThreads;           // pairs per routing tile
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopk = 16;
+
+// Control words at the start of the workspace.
+enum { kCtrlTicket = 0, kCtrlError = 1, kCtrlWords = 64 };
+
+// ---------------------------------------------------------------------------
+// Small wave helpers
+// ---------------------------------------------------------------------------
+
+__device__ inline int lanes_below(uint64_t mask)
+{
+    // number of set bits of `mask` in lanes below this one
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+__device__ inline int wave_inclusive_sum(int v, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int u = __shfl_up(v, d, kWave);
+        if (lane >= d)
+            v += u;
+    }
+    return v;
+}
+
+__device__ inline int read_lane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+
+__device__ inline float read_lane_f(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------
+// Routing: histogram, exclusive scan, stable in-tile ranks
+// ---------------------------------------------------------------------------
+//
+// Pair p = t*K + k belongs to tile p / kRouteTile.  Each block ranks its tile:
+// inside a wave, lanes with the same expert are found by ballots over the bits
+// of the expert id (a match-any), the rank inside the wave is the number of
+// matching lower lanes, and the rank inside the tile adds the counts of the
+// same expert in lower waves.  The block then publishes its tile histogram;
+// the block that finishes last (ticket counter) scans the [tiles x experts]
+// table: expert_off = exclusive scan of the expert totals, and in place of
+// each count the first slot of that expert's run inside that tile.  Slot of
+// pair p = table[tile(p)][e] + rank_in_tile[p]: experts ascending, pairs in
+// ascending p inside an expert.
+
+struct RouteArgs {
+    const int32_t *indices;  // [n_pairs]
+    int32_t n_pairs;
+    int32_t num_experts;
+    int32_t num_ranks;
+    int32_t key_bits;        // bits that hold any expert id < num_experts
+    int32_t *tile_table;     // [tiles][E]: counts, then first slot per (tile, e)
+    int32_t *rank_in_tile;   // [n_pairs], -1 for an invalid id
+    int32_t *expert_off;     // [E+1]
+    int32_t *rank_off;       // [R+1]
+    int32_t *recv_count;     // [R]
+    uint32_t *ctrl;          // [kCtrlWords]
+};
+
+// LDS ints the routing kernel needs for E experts.
+__host__ __device__ inline int route_lds_ints(int E)
+{
+    int a = kRouteWaves * E;
+    int b = kRouteThreads + E + 1;
+    return a > b ? a : b;
+}
+
+// Exclusive prefix sum over the block (kRouteThreads threads, one value each).
+__device__ inline int block_exclusive_sum(int v, int *wave_tot /* kRouteWaves+1 */, int *total)
+{
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int incl = wave_inclusive_sum(v, lane);
+    if (lane == kWave - 1)
+        wave_tot[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        int t = lane < kRouteWaves ? wave_tot[lane] : 0;
+        int ti = wave_inclusive_sum(t, lane);
+        if (lane < kRouteWaves)
+            wave_tot[lane] = ti - t;
+        if (lane == kRouteWaves - 1)
+            wave_tot[kRouteWaves] = ti;
+    }
+    __syncthreads();
+    *total = wave_tot[kRouteWaves];
+    return wave_tot[wave] + incl - v;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a)
+{
+    extern __shared__ int32_t lds[];
+    __shared__ int32_t s_wave_tot[kRouteWaves + 1];
+    __shared__ int32_t s_last;
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int E = a.num_experts;
+    const int tile = blockIdx.x;
+    const int p = tile * kRouteTile + tid;
+    int32_t *wave_cnt = lds;  // [kRouteWaves][E]
+
+    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads)
+        wave_cnt[i] = 0;
+
+    int e = -1;
+    if (p < a.n_pairs) {
+        const int v = a.indices[p];
+        if (v >= 0 && v < E)
+            e = v;
+        else
+            atomicOr(&a.ctrl[kCtrlError], 1u);
+    }
+    const bool valid = e >= 0;
+
+    // match-any over the expert id bits
+    uint64_t match = __ballot(valid);
+    for (int bit = 0; bit < a.key_bits; ++bit) {
+        const bool one = (e >> bit) & 1;
+        const uint64_t ones = __ballot(one);
+        match &= one ? ones : ~ones;
+    }
+    const int rank_in_wave = lanes_below(match);
+
+    __syncthreads();  // wave_cnt cleared
+    if (valid && rank_in_wave == 0)
+        wave_cnt[wave * E + e] = __popcll(match);
+    __syncthreads();
+
+    // per expert: exclusive prefix over the waves, and the tile total
+    for (int x = tid; x < E; x += kRouteThreads) {
+        int run = 0;
+        for (int w = 0; w < kRouteWaves; ++w) {
+            const int c = wave_cnt[w * E + x];
+            wave_cnt[w * E + x] = run;
+            run += c;
+        }
+        a.tile_table[(size_t)tile * E + x] = run;
+    }
+    __syncthreads();
+    if (p < a.n_pairs)
+        a.rank_in_tile[p] = valid ? wave_cnt[wave * E + e] + rank_in_wave : -1;
+
+    // Publish the tile; the last block to arrive does the scan.
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t ticket = atomicAdd(&a.ctrl[kCtrlTicket], 1u);
+        s_last = ticket == gridDim.x - 1;
+        __threadfence();
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+    __threadfence();
+
+    const int B = gridDim.x;
+    int G = kRouteThreads / E;  // threads per expert column, >= 1 since E <= 512
+    if (G > B)
+        G = B;
+    const int chunk = (B + G - 1) / G;
+    int32_t *part = lds;                   // [G][E], G*E <= kRouteThreads
+    int32_t *eoff = lds + kRouteThreads;   // [E+1]
+
+    for (int x = tid; x < G * E; x += kRouteThreads) {
+        const int g = x / E, col = x - g * E;
+        const int b0 = g * chunk;
+        const int b1 = min(B, b0 + chunk);
+        int sum = 0;
+#pragma unroll 8
+        for (int b = b0; b < b1; ++b)
+            sum += a.tile_table[(size_t)b * E + col];
+        part[x] = sum;
+    }
+    __syncthreads();
+
+    int col_total = 0;
+    if (tid < E) {
+        int run = 0;
+        for (int g = 0; g < G; ++g) {
+            const int c = part[g * E + tid];
+            part[g * E + tid] = run;
+            run += c;
+        }
+        col_total = run;
+    }
+    int total;
+    const int excl = block_exclusive_sum(col_total, s_wave_tot, &total);
+    if (tid < E) {
+        eoff[tid] = excl;
+        a.expert_off[tid] = excl;
+    }
+    if (tid == 0) {
+        eoff[E] = total;
+        a.expert_off[E] = total;
+    }
+    __syncthreads();
+
+    const int R = a.num_ranks;
+    const int per_rank = E / R;
+    if (tid <= R)
+        a.rank_off[tid] = eoff[tid * per_rank];
+    if (tid < R)
+        a.recv_count[tid] = eoff[(tid + 1) * per_rank] - eoff[tid * per_rank];
+
+    for (int x = tid; x < G * E; x += kRouteThreads) {
+        const int g = x / E, col = x - g * E;
+        const int b0 = g * chunk;
+        const int b1 = min(B, b0 + chunk);
+        int run = eoff[col] + part[x];
+        for (int b = b0; b < b1; ++b) {
+            const size_t i = (size_t)b * E + col;
+            const int c = a.tile_table[i];
+            a.tile_table[i] = run;
+            run += c;
+        }
+    }
+    if (tid == 0)
+        a.ctrl[kCtrlTicket] = 0;  // re-armed for the next dispatch
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch scatter: one wave per token
+// ---------------------------------------------------------------------------
+
+struct ScatterArgs {
+    int32_t num_tokens;
+    int32_t n_pairs;             // num_tokens * topk: every slot is below this
+    int32_t topk;
+    int32_t num_experts;
+    int32_t hidden;              // bf16 elements per row (quantizing kernels)
+    const int32_t *indices;      // [T, K]
+    const int32_t *tile_table;   // first slot per (tile, expert)
+    const int32_t *rank_in_tile; // [T*K]
+    int32_t *slot_of;            // [T*K]
+    int32_t *src_pos;            // [N_cap]
+    const uint8_t *input;        // [T, in_row_vecs*16]
+    int32_t in_row_vecs;         // 16-byte vectors per input row
+    uint8_t *out;                // [N_cap, out row]
+    const float *weights;        // [T, K] or NULL
+    float *out_weights;          // [N_cap, K]
+    int32_t *out_indices;        // [N_cap, K] or NULL
+    const uint8_t *scales;       // carried [T, scale_words*4] or NULL
+    uint8_t *out_scales;         // [N_cap, scale row] or NULL
+    int32_t scale_words;         // 4-byte words per carried scale row
+    uint32_t *ctrl;              // error flag
+};
+
+// Slot of this lane's pair (lanes < K), also recorded in slot_of / src_pos.
+__device__ inline int pair_slot(const ScatterArgs &a, int t, int lane)
+{
+    int s = -1;
+    if (lane < a.topk) {
+        const int p = t * a.topk + lane;
+        const int r = a.rank_in_tile[p];
+        if (r >= 0) {
+            const int e = a.indices[p];
+            s = a.tile_table[(size_t)(p / kRouteTile) * a.num_experts + e] + r;
+            if ((unsigned)s < (unsigned)a.n_pairs) {
+                a.src_pos[s] = p;
+            } else {
+                // cannot happen for a consistent routing table; never write out of bounds
+                atomicOr(&a.ctrl[kCtrlError], 2u);
+                s = -1;
+            }
+        }
+        a.slot_of[p] = s;
+    }
+    return s;
+}
+
+// Copy the token's weights / indices / carried-scale rows to each of its
+// slots.  All lanes execute the shuffles; stores are predicated.
+__device__ inline void carry_small_rows(const ScatterArgs &a, int t, int slot, int lane)
+{
+    const int K = a.topk;
+    const int kk = K * K;
+    for (int base = 0; base < kk; base += kWave) {
+        const int q = base + lane;
+        const int k = min(q / K, K - 1);
+        const int j = q - (q / K) * K;
+        const int s = __shfl(slot, k, kWave);
+        if (q < kk && s >= 0) {
+            if (a.out_weights)
+                a.out_weights[(size_t)s * K + j] = a.weights[(size_t)t * K + j];
+            if (a.out_indices)
+                a.out_indices[(size_t)s * K + j] = a.indices[(size_t)t * K + j];
+        }
+    }
+    if (a.scales) {
+        const int W = a.scale_words;
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(a.scales) + (size_t)t * W;
+        uint32_t *dst = reinterpret_cast<uint32_t *>(a.out_scales);
+        const int n = K * W;
+        for (int base = 0; base < n; base += kWave) {
+            const int q = base + lane;
+            const int k = min(q / W, K - 1);
+            const int j = q - (q / W) * W;
+            const int s = __shfl(slot, k, kWave);
+            if (q < n && s >= 0)
+                dst[(size_t)s * W + j] = src[j];
+        }
+    }
+}
+
+// bf16 or raw rows: read once, write K times (16-byte nontemporal stores).
+template <int CH>
+__global__ __launch_bounds__(256) void k_scatter_copy(ScatterArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (t >= a.num_tokens)
+        return;
+    const int slot = pair_slot(a, t, lane);
+    carry_small_rows(a, t, slot, lane);
+
+    const int V = a.in_row_vecs;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)t * V;
+    u32x4 *out = reinterpret_cast<u32x4 *>(a.out);
+    for (int base = 0; base < V; base += kWave * CH) {
+        u32x4 v[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int j = base + lane + kWave * i;
+            if (j < V)
+                v[i] = src[j];
+        }
+        for (int k = 0; k < a.topk; ++k) {
+            const int s = read_lane(slot, k);
+            if (s < 0)
+                continue;
+            u32x4 *dst = out + (size_t)s * V;
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int j = base + lane + kWave * i;
+                if (j < V)
+                    __builtin_nontemporal_store(v[i], dst + j);
+            }
+        }
+    }
+}
+
+// OCP E4M3 with one fp32 scale per 128 elements (16 lanes x 8 elements).
+template <int CH>
+__global__ __launch_bounds__(256) void k_scatter_fp8(ScatterArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (t >= a.num_tokens)
+        return;
+    const int slot = pair_slot(a, t, lane);
+    carry_small_rows(a, t, slot, lane);
+
+    const int V = a.hidden / 8;          // 8 bf16 per vector
+    const int nblk = a.hidden / 128;     // scales per row
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)t * V;
+    for (int base = 0; base < V; base += kWave * CH) {
+        u32x2 code[CH];
+        float scale[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int j = base + lane + kWave * i;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (j < V)
+                v = src[j];
+            float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                          bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+            float m = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                m = fmaxf(m, fabsf(x[q]));
+            // V is a multiple of 16, so the 16 lanes of a block are all in or all out
+            m = fmaxf(m, __shfl_xor(m, 1, kWave));
+            m = fmaxf(m, __shfl_xor(m, 2, kWave));
+            m = fmaxf(m, __shfl_xor(m, 4, kWave));
+            m = fmaxf(m, __shfl_xor(m, 8, kWave));
+            float s = 0.0f;
+            uint32_t lo = 0, hi = 0;
+            if (m != 0.0f) {
+                s = m / 448.0f;  // IEEE division, round to nearest
+                lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] / s, x[1] / s, lo, false);
+                lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] / s, x[3] / s, lo, true);
+                hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] / s, x[5] / s, hi, false);
+                hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] / s, x[7] / s, hi, true);
+            }
+            code[i] = u32x2{lo, hi};
+            scale[i] = s;
+        }
+        for (int k = 0; k < a.topk; ++k) {
+            const int s = read_lane(slot, k);
+            if (s < 0)
+                continue;
+            u32x2 *dst = reinterpret_cast<u32x2 *>(a.out + (size_t)s * a.hidden);
+            float *dsc = reinterpret_cast<float *>(a.out_scales) + (size_t)s * nblk;
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int j = base + lane + kWave * i;
+                if (j < V) {
+                    __builtin_nontemporal_store(code[i], dst + j);
+                    if ((lane & 15) == 0)
+                        dsc[j >> 4] = scale[i];
+                }
+            }
+        }
+    }
+}
+
+// MXFP4: E2M1 pairs via v_cvt_scalef32_pk_fp4_f32, one E8M0 scale per 32
+// elements (4 lanes x 8 elements).
+template <int CH>
+__global__ __launch_bounds__(256) void k_scatter_mxfp4(ScatterArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (t >= a.num_tokens)
+        return;
+    const int slot = pair_slot(a, t, lane);
+    carry_small_rows(a, t, slot, lane);
+
+    const int V = a.hidden / 8;
+    const int nblk = a.hidden / 32;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)t * V;
+    for (int base = 0; base < V; base += kWave * CH) {
+        uint32_t code[CH];
+        uint32_t sbyte[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int j = base + lane + kWave * i;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (j < V)
+                v = src[j];
+            float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                          bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+            float m = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                m = fmaxf(m, fabsf(x[q]));
+            m = fmaxf(m, __shfl_xor(m, 1, kWave));
+            m = fmaxf(m, __shfl_xor(m, 2, kWave));
+            // E8M0 byte = floor(log2 amax) - 2 + 127, clamped at 0: the fp32
+            // exponent field minus 2 (0 for zero or subnormal amax)
+            const uint32_t ef = (__float_as_uint(m) >> 23) & 0xFFu;
+            const uint32_t sb = ef > 2u ? ef - 2u : 0u;
+            const float scale = __uint_as_float(sb << 23);  // 2^(sb-127), exponent field only
+            uint32_t q = 0;
+            q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, x[0], x[1], scale, 0);
+            q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, x[2], x[3], scale, 1);
+            q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, x[4], x[5], scale, 2);
+            q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, x[6], x[7], scale, 3);
+            code[i] = q;
+            sbyte[i] = sb;
+        }
+        for (int k = 0; k < a.topk; ++k) {
+            const int s = read_lane(slot, k);
+            if (s < 0)
+                continue;
+            uint32_t *dst = reinterpret_cast<uint32_t *>(a.out + (size_t)s * (a.hidden / 2));
+            uint8_t *dsc = a.out_scales + (size_t)s * nblk;
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int j = base + lane + kWave * i;
+                if (j < V) {
+                    __builtin_nontemporal_store(code[i], dst + j);
+                    if ((lane & 3) == 0)
+                        dsc[j >> 2] = (uint8_t)sbyte[i];
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: one wave per token, gather K rows, fp32 weighted sum, bf16 out
+// ---------------------------------------------------------------------------
+
+struct CombineArgs {
+    int32_t num_tokens;
+    int32_t topk;
+    int32_t row_vecs;        // 16-byte vectors per bf16 row (H/8)
+    const int32_t *slot_of;  // [T*K]
+    const uint8_t *input;    // [N_cap, H] bf16
+    const float *weights;    // [N_cap, K] or NULL
+    uint8_t *output;         // [T, H] bf16
+    float *out_weights;      // [T, K] or NULL
+};
+
+__device__ inline uint32_t pack_bf16_rne(float lo, float hi)
+{
+    const bf16x2 b = __builtin_convertvector(f32x2{lo, hi}, bf16x2);  // v_cvt_pk_bf16_f32
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+// KT = K (compile time) or kMaxTopk with the runtime K as bound.
+template <int KT, int CH>
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a)
+{
+#pragma clang fp contract(off)
+    const int lane = threadIdx.x & (kWave - 1);
+    const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (t >= a.num_tokens)
+        return;
+    const int K = a.topk;
+    int my_slot = -1;
+    float my_w = 0.0f;
+    if (lane < K) {
+        const int p = t * K + lane;
+        my_slot = a.slot_of[p];
+        if (my_slot >= 0)
+            my_w = a.weights ? a.weights[(size_t)my_slot * K + lane] : 1.0f;
+        if (a.out_weights)
+            a.out_weights[p] = my_w;
+    }
+    int slot[KT];
+    float w[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        slot[k] = (k < K) ? read_lane(my_slot, k) : -1;
+        w[k] = (k < K) ? read_lane_f(my_w, k) : 0.0f;
+    }
+
+    const int V = a.row_vecs;
+    const u32x4 *in = reinterpret_cast<const u32x4 *>(a.input);
+    u32x4 *out = reinterpret_cast<u32x4 *>(a.output) + (size_t)t * V;
+    for (int base = 0; base < V; base += kWave * CH) {
+        u32x4 v[KT][CH];
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+#pragma unroll
+            for (int i = 0; i < CH; ++i) {
+                const int j = base + lane + kWave * i;
+                if (slot[k] >= 0 && j < V)
+                    v[k][i] = in[(size_t)slot[k] * V + j];
+                else
+                    v[k][i] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            float acc[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                acc[q] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KT; ++k) {
+                if (slot[k] < 0)
+                    continue;
+                const float wk = w[k];
+                const u32x4 x = v[k][i];
+                acc[0] = acc[0] + wk * bf16_lo(x.x);
+                acc[1] = acc[1] + wk * bf16_hi(x.x);
+                acc[2] = acc[2] + wk * bf16_lo(x.y);
+                acc[3] = acc[3] + wk * bf16_hi(x.y);
+                acc[4] = acc[4] + wk * bf16_lo(x.z);
+                acc[5] = acc[5] + wk * bf16_hi(x.z);
+                acc[6] = acc[6] + wk * bf16_lo(x.w);
+                acc[7] = acc[7] + wk * bf16_hi(x.w);
+            }
+            const int j = base + lane + kWave * i;
+            if (j < V) {
+                const u32x4 r = {pack_bf16_rne(acc[0], acc[1]), pack_bf16_rne(acc[2], acc[3]),
+                                 pack_bf16_rne(acc[4], acc[5]), pack_bf16_rne(acc[6], acc[7])};
+                out[j] = r;
+            }
+        }
+    }
+}
+
+}  // namespace epdc

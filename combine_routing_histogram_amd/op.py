@@ -1,0 +1,223 @@
+"""EpDispatchCombineConfig / EpDispatchCombineOp: the MORI-EP method surface
+(MORI "Communication APIs" page, MORI-EP section, methods table) on top of the
+C ABI.  PyTorch provides device memory and the current HIP stream; every step
+of dispatch and combine runs in the HIP kernels behind libepdc.so.
+
+Receive buffers are allocated once per op at capacity (max_tokens * topk rows)
+-- the analogue of MORI's pre-registered buffers -- and dispatch/combine
+return views of them without synchronizing the host.  Rows
+[rank_off[r], rank_off[r+1]) of every received tensor belong to virtual rank r;
+only the first sum(recv_count) rows are written by a dispatch.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Tuple
+
+import torch
+
+from . import binding as B
+
+QUANT = {"none": B.EPDC_QUANT_NONE, "fp8_e4m3_b128": B.EPDC_QUANT_FP8_E4M3_B128,
+         "mxfp4_b32": B.EPDC_QUANT_MXFP4_B32}
+
+
+@dataclasses.dataclass
+class EpDispatchCombineConfig:
+    max_tokens: int
+    hidden: int
+    topk: int
+    num_experts: int
+    num_ranks: int
+    quant: str = "none"            # "none", "fp8_e4m3_b128", "mxfp4_b32"
+    raw_row_bytes: int = 0         # > 0: dispatch carries opaque byte rows
+    scale_row_bytes: int = 0       # bytes of a carried per-token scale row
+
+    def to_c(self) -> B.epdc_config:
+        kind = B.EPDC_IN_RAW if self.raw_row_bytes > 0 else B.EPDC_IN_BF16
+        return B.make_config(self.max_tokens, self.hidden, self.topk, self.num_experts,
+                             self.num_ranks, kind, QUANT[self.quant], self.raw_row_bytes,
+                             self.scale_row_bytes)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+class EpDispatchCombineOp:
+    def __init__(self, config: EpDispatchCombineConfig, device: Optional[torch.device] = None):
+        self.config = config
+        self.device = torch.device(device) if device is not None else torch.device(
+            "cuda", torch.cuda.current_device())
+        c = config.to_c()
+        self._c = c
+        ws_bytes = B.epdc_workspace_bytes(c)
+        self.payload_row_bytes, self.scale_row_bytes = B.epdc_row_bytes(c)
+        n_cap = config.max_tokens * config.topk
+        self.n_cap = n_cap
+        dev = self.device
+        with torch.cuda.device(dev):
+            self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            self._out = torch.empty((n_cap, self.payload_row_bytes), dtype=torch.uint8, device=dev)
+            self._out_weights = torch.empty((n_cap, config.topk), dtype=torch.float32, device=dev)
+            self._out_indices = torch.empty((n_cap, config.topk), dtype=torch.int32, device=dev)
+            self._out_scales = (torch.empty((n_cap, self.scale_row_bytes), dtype=torch.uint8,
+                                            device=dev) if self.scale_row_bytes else None)
+            self._recv_count = torch.empty(config.num_ranks, dtype=torch.int32, device=dev)
+            self._combined = torch.empty((config.max_tokens, config.hidden), dtype=torch.bfloat16,
+                                         device=dev)
+            self._combined_weights = torch.empty((config.max_tokens, config.topk),
+                                                 dtype=torch.float32, device=dev)
+            self._combine_in = None
+            self._op = B.epdc_create(c, self.workspace.data_ptr(), ws_bytes)
+        self._tokens = 0
+        self._scales_dtype = None
+
+    def __del__(self):
+        op = getattr(self, "_op", None)
+        if op:
+            try:
+                B.epdc_destroy(op)
+            except Exception:
+                pass
+            self._op = None
+
+    # ---- helpers -------------------------------------------------------------------
+    def _stream(self) -> int:
+        return torch.cuda.current_stream(self.device).cuda_stream
+
+    def _need(self, t: torch.Tensor, name: str, dtype=None, shape=None):
+        if t.device != self.device:
+            raise ValueError(f"{name} is on {t.device}, op is on {self.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+    def _ws_view(self, ptr: int, count: int) -> torch.Tensor:
+        off = ptr - self.workspace.data_ptr()
+        return self.workspace[off:off + 4 * count].view(torch.int32)
+
+    # ---- methods table ---------------------------------------------------------------
+    def dispatch(self, input: torch.Tensor, weights: Optional[torch.Tensor],
+                 scales: Optional[torch.Tensor], indices: torch.Tensor):
+        """Route tokens to expert slots.
+
+        Returns (output, weights, scales, indices, recv_count) as views of the
+        op's capacity-sized receive buffers (scales is None when there are
+        none).  output is bf16 [N_cap, H] for bf16 input, float8_e4m3fn
+        [N_cap, H] for FP8, uint8 [N_cap, H/2] (packed E2M1) for MXFP4, or
+        uint8 [N_cap, raw_row_bytes] for raw rows.
+        """
+        cfg = self.config
+        T = int(indices.shape[0])
+        self._need(indices, "indices", torch.int32, (T, cfg.topk))
+        if cfg.raw_row_bytes:
+            self._need(input, "input")
+            if input.numel() * input.element_size() != T * cfg.raw_row_bytes:
+                raise ValueError("input must hold raw_row_bytes per token")
+        else:
+            self._need(input, "input", torch.bfloat16, (T, cfg.hidden))
+        if weights is not None:
+            self._need(weights, "weights", torch.float32, (T, cfg.topk))
+        if scales is not None:
+            self._need(scales, "scales")
+            if scales.numel() * scales.element_size() != T * cfg.scale_row_bytes:
+                raise ValueError("scales must hold scale_row_bytes per token")
+            self._scales_dtype = scales.dtype
+        B.epdc_dispatch(self._op, self._stream(), T, _ptr(input), _ptr(weights), _ptr(scales),
+                        _ptr(indices), _ptr(self._out),
+                        _ptr(self._out_weights) if weights is not None else 0,
+                        _ptr(self._out_scales) if (scales is not None or cfg.quant != "none") else 0,
+                        _ptr(self._out_indices), _ptr(self._recv_count))
+        self._tokens = T
+        return (self.received_payload(),
+                self._out_weights if weights is not None else None,
+                self.received_scales(scales is not None),
+                self._out_indices, self._recv_count)
+
+    def received_payload(self) -> torch.Tensor:
+        cfg = self.config
+        if cfg.raw_row_bytes:
+            return self._out
+        if cfg.quant == "none":
+            return self._out.view(torch.bfloat16)
+        if cfg.quant == "fp8_e4m3_b128":
+            return self._out.view(torch.float8_e4m3fn)
+        return self._out
+
+    def received_scales(self, carried: bool = True) -> Optional[torch.Tensor]:
+        cfg = self.config
+        if cfg.quant == "fp8_e4m3_b128":
+            return self._out_scales.view(torch.float32)
+        if cfg.quant == "mxfp4_b32":
+            return self._out_scales
+        if not carried or self._out_scales is None:
+            return None
+        dt = self._scales_dtype or torch.uint8
+        return self._out_scales.view(dt)
+
+    def combine(self, input: torch.Tensor, weights: Optional[torch.Tensor] = None,
+                indices: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+        """Weighted gather of the expert outputs back to token order.
+
+        input: bf16 [n, H] in the received layout with n >= T*K of the last
+        dispatch (e.g. the dispatch output itself); weights: fp32 [n, K] in
+        the received layout or None.  Returns (output bf16 [T, H], weights fp32 [T, K]).
+        """
+        cfg = self.config
+        self._need(input, "input", torch.bfloat16)
+        if input.dim() != 2 or input.shape[1] != cfg.hidden:
+            raise ValueError("combine input must be [rows, hidden] bf16")
+        rows = self._tokens * cfg.topk          # received rows are a prefix of these
+        if input.shape[0] < rows:
+            raise ValueError(f"combine input needs at least {rows} rows")
+        if weights is not None:
+            self._need(weights, "weights", torch.float32)
+            if weights.dim() != 2 or weights.shape[0] < rows or weights.shape[1] != cfg.topk:
+                raise ValueError(f"combine weights must be [>= {rows}, topk] fp32")
+        B.epdc_combine(self._op, self._stream(), _ptr(input), _ptr(weights), _ptr(indices),
+                       _ptr(self._combined), _ptr(self._combined_weights))
+        T = self._tokens
+        return self._combined[:T], self._combined_weights[:T]
+
+    def reset(self) -> None:
+        B.epdc_reset(self._op)
+        self._tokens = 0
+
+    def get_dispatch_src_token_pos(self) -> torch.Tensor:
+        """Per received row, the pair index t*K + k it came from (the first
+        sum(recv_count) entries are meaningful)."""
+        ptr, n = B.epdc_get_dispatch_src_token_pos(self._op)
+        return self._ws_view(ptr, n)
+
+    def get_routing(self):
+        """(expert_off [E+1], rank_off [R+1], slot_of [T*K]) of the last dispatch."""
+        a, b, c = B.epdc_get_routing(self._op)
+        cfg = self.config
+        return (self._ws_view(a, cfg.num_experts + 1), self._ws_view(b, cfg.num_ranks + 1),
+                self._ws_view(c, self._tokens * cfg.topk))
+
+    def get_registered_combine_input_buffer(self, dtype=torch.bfloat16) -> torch.Tensor:
+        """A capacity-sized [N_cap, H] buffer owned by the op, for expert outputs."""
+        if dtype != torch.bfloat16:
+            raise ValueError("combine input is bf16")
+        if self._combine_in is None:
+            self._combine_in = torch.empty((self.n_cap, self.config.hidden), dtype=torch.bfloat16,
+                                           device=self.device)
+        return self._combine_in
+
+    def device_error(self) -> int:
+        """Synchronize and return/clear the sticky bad-expert-id flag."""
+        return B.epdc_get_device_error(self._op, self._stream())
+
+    # ---- timing ------------------------------------------------------------------------
+    def profile_begin(self, max_launches: int) -> None:
+        B.epdc_profile_begin(self._op, max_launches)
+
+    def profile_end(self):
+        """{kernel name: (total ms, launches)} for the launches since profile_begin."""
+        ms, n = B.epdc_profile_end(self._op)
+        return {B.epdc_kernel_name(k): (ms[k], n[k]) for k in range(B.EPDC_NUM_KERNELS) if n[k]}

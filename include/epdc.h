@@ -1,0 +1,222 @@
+/*
+ * epdc.h -- C ABI of the MI355X (gfx950) MoE expert-parallel dispatch/combine
+ * hot path.
+ *
+ * The operations mirror the methods of MORI's EpDispatchCombineOp (MORI
+ * "Communication APIs" page, MORI-EP section, methods table):
+ *   dispatch(input, weights, scales, indices)
+ *       -> (output, weights, scales, indices, recv_count)
+ *   combine(input, weights, indices) -> (output, weights)
+ *   reset()
+ *   get_dispatch_src_token_pos()
+ * on one GPU, for one GPU's share of the tokens, with the destination ranks
+ * of an intra-node EP group modelled as contiguous segments of one receive
+ * buffer in HBM.
+ *
+ * Received layout.  Every (token t, k) pair with a valid expert index gets one
+ * received row ("slot").  Slots are grouped by expert, experts ascending, and
+ * inside an expert ordered by the pair index p = t*K + k.  Virtual rank r owns
+ * experts [r*E/R, (r+1)*E/R), i.e. the slots [rank_off[r], rank_off[r+1]).
+ * recv_count[r] = rank_off[r+1] - rank_off[r] is produced by dispatch itself,
+ * zero included (same page, "AsyncLL v2 SDMA overlap" section: the receive
+ * side writes the total including zero; dispatch kernels produce the count).
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are HBM addresses on the op's device; the
+ *    caller allocates and owns all of them, including the op's workspace.  The
+ *    library never allocates device memory.  "host" pointers are read or
+ *    written before the call returns.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the null stream.  The
+ *    work is enqueued on it and the call returns without waiting; results are
+ *    valid once that work completes (same page, AsyncLL section: data and
+ *    counts are ready after the receive phase completes on the stream).
+ *  - Row-major layouts; no padding between rows.  Payload rows (input, out,
+ *    output) start 16-byte aligned, every other array 4-byte aligned;
+ *    misaligned pointers give EPDC_ERR_INVALID_ARGS.
+ *  - A non-SUCCESS status leaves no work enqueued, except EPDC_ERR_GPU_OP
+ *    after a failed launch.  epdc_last_error() gives a thread-local message.
+ *  - An op is not thread-safe and its calls must be ordered (one stream, or
+ *    ordered streams): the workspace holds the routing between calls.
+ * Status names follow MORI-IO's StatusCode enum (same page, MORI-IO section).
+ */
+#ifndef EPDC_H
+#define EPDC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum epdc_status {
+    EPDC_SUCCESS = 0,
+    EPDC_ERR_INVALID_ARGS = -1,  /* bad pointer, size or configuration */
+    EPDC_ERR_BAD_STATE = -2,     /* e.g. combine with no dispatch recorded */
+    EPDC_ERR_GPU_OP = -3,        /* a HIP call failed (message says which) */
+    EPDC_ERR_UNSUPPORTED = -4,   /* device is not gfx950 */
+    EPDC_ERR_NOT_FOUND = -5      /* unknown kernel id */
+} epdc_status;
+
+/* Payload kind of dispatch's `input`.  RAW rows are opaque bytes that are
+ * copied unchanged, e.g. already-quantized FP8/FP4 payloads ("Choosing an EP
+ * API and backend" page, "EP paths" table, HIP row). */
+typedef enum epdc_input_kind {
+    EPDC_IN_BF16 = 0,            /* [T, hidden] bfloat16 */
+    EPDC_IN_RAW = 1              /* [T, raw_row_bytes] bytes */
+} epdc_input_kind;
+
+/* On-the-fly quantization applied by dispatch to BF16 input ("Choosing an EP
+ * API and backend" page, EPv2 restrictions list: OCP E4M3 on gfx950; FP4 via
+ * gfx950's pair-at-a-time scaled convert family). */
+typedef enum epdc_quant {
+    EPDC_QUANT_NONE = 0,
+    /* OCP E4M3 codes [N, H] + fp32 scales [N, H/128]; per block of 128:
+     * scale = amax/448 (fp32 division), code = E4M3(x/scale) rounded to
+     * nearest even, saturated to +-448; amax == 0 gives scale 0, codes 0. */
+    EPDC_QUANT_FP8_E4M3_B128 = 1,
+    /* MXFP4: E2M1 codes two per byte (element 2m in the low nibble of byte
+     * m) [N, H/2] + E8M0 scales [N, H/32]; per block of 32 the shared
+     * exponent is floor(log2(amax)) - 2 clamped to [-127, 127] (-127 for an
+     * all-zero block); codes round to nearest even and saturate to +-6. */
+    EPDC_QUANT_MXFP4_B32 = 2
+} epdc_quant;
+
+/* Fixed at creation. */
+typedef struct epdc_config {
+    int32_t max_tokens;      /* T_max >= 0: largest num_tokens of a dispatch */
+    int32_t hidden;          /* H > 0, multiple of 8 (bf16 rows of 16-byte
+                                vectors); multiple of 128 for FP8, 32 for MXFP4 */
+    int32_t topk;            /* K in [1, 16] */
+    int32_t num_experts;     /* E in [1, 512] */
+    int32_t num_ranks;       /* R >= 1 with E % R == 0 */
+    int32_t input_kind;      /* epdc_input_kind */
+    int32_t quant;           /* epdc_quant; != NONE requires EPDC_IN_BF16 */
+    int32_t raw_row_bytes;   /* EPDC_IN_RAW: bytes per row, > 0, multiple of 16 */
+    int32_t scale_row_bytes; /* bytes per carried scale row, multiple of 4,
+                                0 = dispatch carries no scales; must be 0 when
+                                quant != NONE (scales are then produced) */
+} epdc_config;
+
+typedef struct epdc_op epdc_op;
+
+/* Kernel ids for the profiling calls below. */
+enum {
+    EPDC_KERNEL_ROUTE = 0,         /* histogram + scan + in-tile ranks */
+    EPDC_KERNEL_SCATTER = 1,       /* slot + row copy (bf16 or raw) */
+    EPDC_KERNEL_SCATTER_FP8 = 2,   /* slot + E4M3 quantize + copy */
+    EPDC_KERNEL_SCATTER_MXFP4 = 3, /* slot + MXFP4 quantize + copy */
+    EPDC_KERNEL_COMBINE = 4,       /* gather + weighted fp32 sum */
+    EPDC_NUM_KERNELS = 5
+};
+
+/* Bytes of device workspace an op with this config needs (host only, no GPU
+ * call).  Returns EPDC_ERR_INVALID_ARGS for an invalid config. */
+epdc_status epdc_workspace_bytes(const epdc_config *cfg, size_t *bytes);
+
+/* Bytes per received row of dispatch's `out` and `out_scales` for this config
+ * (host only): bf16 2H, RAW raw_row_bytes, FP8 H, MXFP4 H/2; scales
+ * scale_row_bytes, 4*H/128 for FP8, H/32 for MXFP4. */
+epdc_status epdc_row_bytes(const epdc_config *cfg, size_t *payload_bytes,
+                           size_t *scale_bytes);
+
+/* Create an op on the current HIP device.  `workspace` (device, >= the size
+ * from epdc_workspace_bytes, 256-byte aligned) stays owned by the caller and
+ * must outlive the op; the op clears its control words synchronously.
+ * EPDC_ERR_UNSUPPORTED if the current device is not gfx950. */
+epdc_status epdc_create(const epdc_config *cfg, void *workspace,
+                        size_t workspace_bytes, epdc_op **op);
+
+/* Free the host-side op (the workspace is the caller's). NULL is allowed. */
+epdc_status epdc_destroy(epdc_op *op);
+
+/*
+ * dispatch: route num_tokens tokens to their top-K experts' slots.
+ *   input       device [T, H] bf16 (EPDC_IN_BF16) or [T, raw_row_bytes] (RAW)
+ *   weights     device [T, K] fp32, or NULL (then out_weights must be NULL)
+ *   scales      device [T, scale_row_bytes] carried unchanged, or NULL; must
+ *               be NULL when scale_row_bytes == 0 or quant != NONE
+ *   indices     device [T, K] int32 expert ids.  An id outside [0, E) is a
+ *               precondition violation: that pair gets no slot, the device
+ *               error flag is raised (epdc_get_device_error), nothing is
+ *               written out of bounds.  (Flag bit 1; bit 2 marks a slot
+ *               outside [0, num_tokens*K), which a consistent routing table
+ *               never produces: such a pair is dropped, not written.)
+ *   out         device [T_max*K, payload row] (epdc_row_bytes)
+ *   out_weights device [T_max*K, K] fp32 (each slot carries its token's row)
+ *   out_scales  device [T_max*K, scale row]; required when quant != NONE or
+ *               scales != NULL, else ignored
+ *   out_indices device [T_max*K, K] int32, or NULL
+ *   recv_count  device [R] int32 (rows per virtual rank; sum = valid pairs)
+ * With num_tokens == 0 only out and recv_count are required (recv_count and
+ * the offsets are written as zeros).
+ * Only rows [0, n_valid) of the outputs are written, n_valid = expert_off[E].
+ * Records the routing for the next combine and for the getters below.
+ */
+epdc_status epdc_dispatch(epdc_op *op, void *stream, int32_t num_tokens,
+                          const void *input, const float *weights,
+                          const void *scales, const int32_t *indices,
+                          void *out, float *out_weights, void *out_scales,
+                          int32_t *out_indices, int32_t *recv_count);
+
+/*
+ * combine: for every token t of the last dispatch,
+ *   output[t, :] = bf16_rne( sum_{k=0..K-1} w(t,k) * input[slot(t,k), :] )
+ * accumulated in fp32 in k order (a separate multiply and add per term,
+ * starting from +0), with w(t,k) = weights[slot(t,k), k] (1 if weights is
+ * NULL).  Pairs without a slot contribute nothing and report weight 0.
+ *   input       device [rows, H] bf16 in the received layout; only rows below
+ *               n_valid <= num_tokens*K of the last dispatch are read
+ *   weights     device [rows, K] fp32 in the received layout, or NULL
+ *   indices     device [rows, K] int32 or NULL: accepted for signature
+ *               parity with the pages and not read (the op keeps the routing)
+ *   output      device [num_tokens, H] bf16
+ *   out_weights device [num_tokens, K] fp32 = w(t,k), or NULL
+ * EPDC_ERR_BAD_STATE if no dispatch is recorded (none yet, or reset).
+ */
+epdc_status epdc_combine(epdc_op *op, void *stream, const void *input,
+                         const float *weights, const int32_t *indices,
+                         void *output, float *out_weights);
+
+/* Device pointer to src_token_pos [T_max*K] int32 of the last dispatch: for
+ * slot s < n_valid, the pair index p = t*K + k it came from ("Get source
+ * positions of dispatched tokens (for verification)", methods table).
+ * *count = num_tokens*K of that dispatch (host).  BAD_STATE if none. */
+epdc_status epdc_get_dispatch_src_token_pos(epdc_op *op, const int32_t **dev_ptr,
+                                            int32_t *count);
+
+/* Device pointers into the workspace for the last dispatch: expert_off [E+1],
+ * rank_off [R+1] (exclusive prefix sums), slot_of [num_tokens*K] (slot of
+ * pair p, -1 if none).  Any may be NULL.  BAD_STATE if none. */
+epdc_status epdc_get_routing(epdc_op *op, const int32_t **expert_off,
+                             const int32_t **rank_off, const int32_t **slot_of);
+
+/* Wait for `stream`, then return (host) and clear the sticky device error
+ * flag: nonzero if some dispatch since the last call saw an expert id
+ * outside [0, E).  Synchronizes; not for use under graph capture. */
+epdc_status epdc_get_device_error(epdc_op *op, void *stream, int32_t *flag);
+
+/* Forget the recorded routing ("Reset internal state between iterations").
+ * No device work: counts need no clearing because dispatch writes them. */
+epdc_status epdc_reset(epdc_op *op);
+
+/* Thread-local message for the last non-SUCCESS status ("" if none). */
+const char *epdc_last_error(void);
+
+/* Kernel name for an EPDC_KERNEL_* id, NULL if unknown. */
+const char *epdc_kernel_name(int32_t kernel_id);
+
+/* Per-kernel timing with HIP events recorded on the launch stream around
+ * each kernel the op launches.  begin: allocate events for up to
+ * max_launches launches (host-side event objects, no device memory).  end:
+ * wait for the last recorded event, write (host) the summed milliseconds and
+ * the launch count per kernel id into ms[EPDC_NUM_KERNELS] and
+ * launches[EPDC_NUM_KERNELS], and release the events. */
+epdc_status epdc_profile_begin(epdc_op *op, int32_t max_launches);
+epdc_status epdc_profile_end(epdc_op *op, float *ms, int32_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EPDC_H */

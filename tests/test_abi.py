@@ -1,0 +1,129 @@
+"""CPU checks of the C-ABI boundary: the library loads, exports every entry
+point include/epdc.h declares, and its host-only calls (sizes, config
+validation, argument checks) behave as documented.  No GPU work is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from combine_routing_histogram_amd import binding as B
+from combine_routing_histogram_amd import build as hip_build
+from combine_routing_histogram_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if hip_build.is_stale():
+        hip_build.build()
+    return B.lib()
+
+
+def test_exports_every_declared_entry_point(lib):
+    names = B.header_entry_points()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/epdc.h but not exported"
+    assert set(names) == set(B._SIGNATURES), "binding and header disagree"
+
+
+def test_enum_values_match_header():
+    text = open(B.HEADER).read()
+    for name, val in re.findall(r"\b(EPDC_[A-Z0-9_]+)\s*=\s*(-?\d+)", text):
+        assert getattr(B, name) == int(val), name
+
+
+def _cfg(w, **kw):
+    q = {"none": 0, "fp8_e4m3_b128": 1, "mxfp4_b32": 2}[w.quant]
+    args = dict(max_tokens=w.tokens, hidden=w.hidden, topk=w.topk, num_experts=w.experts,
+                num_ranks=w.ranks, quant=q)
+    args.update(kw)
+    return B.make_config(**args)
+
+
+@pytest.mark.parametrize("name", sorted(wl.WORKLOADS))
+def test_workspace_and_row_bytes(lib, name):
+    w = wl.WORKLOADS[name]
+    c = _cfg(w)
+    n = B.epdc_workspace_bytes(c)
+    N = w.tokens * w.topk
+    # control words + tile table + 3 per-pair int arrays + offsets, 256-aligned
+    assert n >= 4 * 3 * N + 4 * (w.experts + 1)
+    assert n % 256 == 0
+    p, s = B.epdc_row_bytes(c)
+    want = {"none": (2 * w.hidden, 0), "fp8_e4m3_b128": (w.hidden, 4 * w.hidden // 128),
+            "mxfp4_b32": (w.hidden // 2, w.hidden // 32)}[w.quant]
+    assert (p, s) == want
+
+
+def test_raw_carry_row_bytes(lib):
+    c = B.make_config(64, 7168, 8, 256, 8, input_kind=B.EPDC_IN_RAW, raw_row_bytes=7168,
+                      scale_row_bytes=224)
+    assert B.epdc_row_bytes(c) == (7168, 224)
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(hidden=100), "hidden"),
+    (dict(topk=0), "topk"),
+    (dict(topk=17), "topk"),
+    (dict(num_experts=513), "num_experts"),
+    (dict(num_ranks=3), "num_ranks"),
+    (dict(max_tokens=-1), "max_tokens"),
+    (dict(quant=1, hidden=64), "128"),
+    (dict(quant=2, hidden=48), "32"),
+    (dict(quant=7), "quant"),
+    (dict(input_kind=1, raw_row_bytes=10), "raw_row_bytes"),
+    (dict(input_kind=1, quant=1, raw_row_bytes=16), "bf16"),
+    (dict(scale_row_bytes=6), "scale_row_bytes"),
+    (dict(quant=1, scale_row_bytes=8), "scale_row_bytes"),
+    (dict(max_tokens=1 << 28, topk=8), "2^30"),
+])
+def test_invalid_configs_rejected(lib, kw, msg):
+    args = dict(max_tokens=128, hidden=256, topk=2, num_experts=8, num_ranks=2)
+    args.update(kw)
+    with pytest.raises(B.EpdcError) as ei:
+        B.epdc_workspace_bytes(B.make_config(**args))
+    assert ei.value.status == B.EPDC_ERR_INVALID_ARGS
+    assert msg in str(ei.value)
+
+
+def test_null_op_and_state_errors(lib):
+    with pytest.raises(B.EpdcError) as ei:
+        B.epdc_dispatch(0, 0, 1, 1, 0, 0, 1, 1, 0, 0, 0, 1)
+    assert ei.value.status == B.EPDC_ERR_INVALID_ARGS
+    with pytest.raises(B.EpdcError) as ei:
+        B.epdc_combine(0, 0, 1, 0, 0, 1, 0)
+    assert ei.value.status == B.EPDC_ERR_INVALID_ARGS
+    with pytest.raises(B.EpdcError):
+        B.epdc_reset(0)
+    assert lib.epdc_destroy(None) == B.EPDC_SUCCESS
+    assert B.epdc_last_error() == ""
+
+
+def test_kernel_names(lib):
+    names = [B.epdc_kernel_name(k) for k in range(B.EPDC_NUM_KERNELS)]
+    assert names == ["k_route", "k_scatter_copy", "k_scatter_fp8", "k_scatter_mxfp4",
+                     "k_combine"]
+    assert B.epdc_kernel_name(B.EPDC_NUM_KERNELS) is None
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libepdc.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        B.lib()
+
+
+def test_product_code_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "combine_routing_histogram_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle|liboracle|epdc_oracle", text,
+                                     flags=re.M), f
+    hdr = open(os.path.join(ROOT, "include", "epdc.h")).read()
+    assert "oracle" not in hdr
