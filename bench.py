@@ -39,7 +39,8 @@ def alg_bytes(kernel: str, w) -> int:
                and src_token_pos (8K)
       combine: read K rows (2KH) + slot_of and the K weights (8K); write
                the row (2H) and its K weights (4K)
-      route:   read the indices (4K); write the in-tile ranks (4K)
+      route:   read the indices (4K); write the in-tile ranks (4K); the scan
+               only touches the small tile table (counted as 0)
     """
     T, H, K = w.tokens, w.hidden, w.topk
     P, Q = {"none": (2 * H, 0), "fp8_e4m3_b128": (H, 4 * H // 128),
@@ -48,8 +49,10 @@ def alg_bytes(kernel: str, w) -> int:
         per = 2 * H + 8 * K + K * (P + Q) + 8 * K * K + 8 * K
     elif kernel == "k_combine":
         per = 2 * K * H + 8 * K + 2 * H + 4 * K
-    elif kernel == "k_route":
+    elif kernel == "k_route_rank":
         per = 8 * K
+    elif kernel == "k_route_scan":
+        return 0
     else:
         raise ValueError(kernel)
     return per * T
@@ -100,6 +103,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="deepseek_v3_bf16")
+    ap.add_argument("--kernel-events", choices=["timed", "separate"], default="timed",
+                    help="record the per-kernel events in the timed steps, or in a second "
+                         "pass of the same number of steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU-oracle baseline (0 = skip)")
     args = ap.parse_args()
@@ -144,7 +150,9 @@ def main() -> int:
 
     stream = torch.cuda.current_stream(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    op.profile_begin(4 * args.steps)
+    timed_events = args.kernel_events == "timed"
+    if timed_events:
+        op.profile_begin(4 * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
@@ -153,6 +161,11 @@ def main() -> int:
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if not timed_events:
+        op.profile_begin(4 * args.steps)
+        for _ in range(args.steps):
+            y, y_w = step()
+        torch.cuda.synchronize()
     prof = op.profile_end()
     ms_step_events = ev0.elapsed_time(ev1) / args.steps
     ms_step = wall * 1e3 / args.steps
@@ -163,8 +176,8 @@ def main() -> int:
         b = alg_bytes(name, w)
         avg = ms / n
         kernels[name] = {"launches": n, "avg_us": avg * 1e3, "alg_bytes": b,
-                         "gbps": b / (avg * 1e-3) / 1e9,
-                         "frac": b / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+                         "gbps": b / (avg * 1e-3) / 1e9 if b else None,
+                         "frac": b / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS if b else None}
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
     dk = kernels[dom]
     # the method's bytes: x read once, K row copies written, K rows read back, one row
@@ -198,6 +211,7 @@ def main() -> int:
                      "traffic": traffic},
         "kernels": kernels,
         "ms_per_step_events": ms_step_events,
+        "kernel_events": args.kernel_events,
     }
     parity = "skipped"
     result["cpu_baseline"] = None

@@ -32,11 +32,12 @@ EPDC_QUANT_FP8_E4M3_B128 = 1
 EPDC_QUANT_MXFP4_B32 = 2
 
 EPDC_KERNEL_ROUTE = 0
-EPDC_KERNEL_SCATTER = 1
-EPDC_KERNEL_SCATTER_FP8 = 2
-EPDC_KERNEL_SCATTER_MXFP4 = 3
-EPDC_KERNEL_COMBINE = 4
-EPDC_NUM_KERNELS = 5
+EPDC_KERNEL_ROUTE_SCAN = 1
+EPDC_KERNEL_SCATTER = 2
+EPDC_KERNEL_SCATTER_FP8 = 3
+EPDC_KERNEL_SCATTER_MXFP4 = 4
+EPDC_KERNEL_COMBINE = 5
+EPDC_NUM_KERNELS = 6
 
 
 class epdc_config(ctypes.Structure):

@@ -137,7 +137,8 @@ void row_bytes_for(const epdc_config &c, size_t *payload, size_t *scales)
 }
 
 const char *const kKernelNames[EPDC_NUM_KERNELS] = {
-    "k_route", "k_scatter_copy", "k_scatter_fp8", "k_scatter_mxfp4", "k_combine"};
+    "k_route_rank", "k_route_scan", "k_scatter_copy", "k_scatter_fp8", "k_scatter_mxfp4",
+    "k_combine"};
 
 }  // namespace
 
@@ -189,10 +190,10 @@ epdc_status launch(epdc_op *op, hipStream_t st, int kernel_id, F &&f)
 // chip with them.
 int waves_per_block(int tokens) { return tokens >= 2048 ? 4 : 1; }
 
-template <int KT, int CH>
+template <int KT>
 void launch_combine(int grid, int block, hipStream_t st, const CombineArgs &a)
 {
-    k_combine<KT, CH><<<grid, block, 0, st>>>(a);
+    k_combine<KT><<<grid, block, 0, st>>>(a);
 }
 
 }  // namespace
@@ -330,6 +331,7 @@ epdc_status epdc_dispatch(epdc_op *op, void *stream, int32_t num_tokens, const v
     ra.num_experts = c.num_experts;
     ra.num_ranks = c.num_ranks;
     ra.key_bits = op->key_bits;
+    ra.tiles = tiles;
     ra.tile_table = op->i32(op->lay.tile_table);
     ra.rank_in_tile = op->i32(op->lay.rank_in_tile);
     ra.expert_off = op->i32(op->lay.expert_off);
@@ -337,9 +339,19 @@ epdc_status epdc_dispatch(epdc_op *op, void *stream, int32_t num_tokens, const v
     ra.recv_count = recv_count;
     ra.ctrl = op->ctrl();
     const size_t lds = sizeof(int32_t) * (size_t)route_lds_ints(c.num_experts);
-    epdc_status s = launch(op, st, EPDC_KERNEL_ROUTE, [&] {
-        k_route<<<tiles, kRouteThreads, lds, st>>>(ra);
-    });
+    epdc_status s;
+    if (tiles == 1) {
+        s = launch(op, st, EPDC_KERNEL_ROUTE, [&] {
+            k_route_rank<true><<<1, kRouteThreads, lds, st>>>(ra);
+        });
+    } else {
+        s = launch(op, st, EPDC_KERNEL_ROUTE, [&] {
+            k_route_rank<false><<<tiles, kRouteThreads, lds, st>>>(ra);
+        });
+        if (s == EPDC_SUCCESS)
+            s = launch(op, st, EPDC_KERNEL_ROUTE_SCAN,
+                       [&] { k_route_scan<<<1, kRouteThreads, 0, st>>>(ra); });
+    }
     if (s != EPDC_SUCCESS)
         return s;
 
@@ -415,6 +427,7 @@ epdc_status epdc_combine(epdc_op *op, void *stream, const void *input, const flo
     ca.num_tokens = T;
     ca.topk = c.topk;
     ca.row_vecs = c.hidden / 8;
+    ca.segs = (ca.row_vecs + kCombineSegVecs - 1) / kCombineSegVecs;
     ca.slot_of = op->i32(op->lay.slot_of);
     ca.input = static_cast<const uint8_t *>(input);
     ca.weights = weights;
@@ -422,17 +435,18 @@ epdc_status epdc_combine(epdc_op *op, void *stream, const void *input, const flo
     ca.out_weights = out_weights;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int wpb = waves_per_block(T);
-    const int grid = (T + wpb - 1) / wpb;
+    const int waves = T * ca.segs;  // one wave per (token, row segment)
+    const int wpb = waves >= 4096 ? 4 : 1;
+    const int grid = (waves + wpb - 1) / wpb;
     const int block = wpb * kWave;
     epdc_status s = launch(op, st, EPDC_KERNEL_COMBINE, [&] {
         switch (c.topk) {
-        case 1: launch_combine<1, 4>(grid, block, st, ca); break;
-        case 2: launch_combine<2, 4>(grid, block, st, ca); break;
-        case 4: launch_combine<4, 2>(grid, block, st, ca); break;
-        case 6: launch_combine<6, 2>(grid, block, st, ca); break;
-        case 8: launch_combine<8, 2>(grid, block, st, ca); break;
-        default: launch_combine<kMaxTopk, 1>(grid, block, st, ca); break;
+        case 1: launch_combine<1>(grid, block, st, ca); break;
+        case 2: launch_combine<2>(grid, block, st, ca); break;
+        case 4: launch_combine<4>(grid, block, st, ca); break;
+        case 6: launch_combine<6>(grid, block, st, ca); break;
+        case 8: launch_combine<8>(grid, block, st, ca); break;
+        default: launch_combine<0>(grid, block, st, ca); break;
         }
     });
     if (s != EPDC_SUCCESS)

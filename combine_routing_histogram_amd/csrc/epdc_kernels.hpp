@@ -34,7 +34,7 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxTopk = 16;
 
 // Control words at the start of the workspace.
-enum { kCtrlTicket = 0, kCtrlError = 1, kCtrlWords = 64 };
+enum { kCtrlError = 1, kCtrlWords = 64 };
 
 // ---------------------------------------------------------------------------
 // Small wave helpers
@@ -72,16 +72,21 @@ __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0
 // Routing: histogram, exclusive scan, stable in-tile ranks
 // ---------------------------------------------------------------------------
 //
-// Pair p = t*K + k belongs to tile p / kRouteTile.  Each block ranks its tile:
-// inside a wave, lanes with the same expert are found by ballots over the bits
-// of the expert id (a match-any), the rank inside the wave is the number of
-// matching lower lanes, and the rank inside the tile adds the counts of the
-// same expert in lower waves.  The block then publishes its tile histogram;
-// the block that finishes last (ticket counter) scans the [tiles x experts]
-// table: expert_off = exclusive scan of the expert totals, and in place of
-// each count the first slot of that expert's run inside that tile.  Slot of
-// pair p = table[tile(p)][e] + rank_in_tile[p]: experts ascending, pairs in
-// ascending p inside an expert.
+// Pair p = t*K + k belongs to tile p / kRouteTile.  k_route_rank ranks each
+// tile in one block: inside a wave, lanes with the same expert are found by
+// ballots over the bits of the expert id (a match-any), the rank inside the
+// wave is the number of matching lower lanes, and the rank inside the tile
+// adds the counts of the same expert in lower waves.  The block writes the
+// tile's expert histogram as one row of a [tiles x experts] table.
+// k_route_scan (one block, next launch on the stream) turns the table into
+// expert_off = exclusive scan of the expert totals and, in place of each
+// count, the first slot of that expert's run inside that tile.  Slot of pair
+// p = table[tile(p)][e] + rank_in_tile[p]: experts ascending, pairs in
+// ascending p inside an expert.  With a single tile the rank kernel scans its
+// own histogram and the second launch is skipped.  The kernel boundary is the
+// only cross-block synchronization: an in-kernel "last block scans" scheme
+// needs agent-scope fences, i.e. L2 writeback/invalidate across the XCDs, and
+// measured slower than the second launch.
 
 struct RouteArgs {
     const int32_t *indices;  // [n_pairs]
@@ -89,6 +94,7 @@ struct RouteArgs {
     int32_t num_experts;
     int32_t num_ranks;
     int32_t key_bits;        // bits that hold any expert id < num_experts
+    int32_t tiles;           // ceil(n_pairs / kRouteTile), >= 1
     int32_t *tile_table;     // [tiles][E]: counts, then first slot per (tile, e)
     int32_t *rank_in_tile;   // [n_pairs], -1 for an invalid id
     int32_t *expert_off;     // [E+1]
@@ -97,13 +103,8 @@ struct RouteArgs {
     uint32_t *ctrl;          // [kCtrlWords]
 };
 
-// LDS ints the routing kernel needs for E experts.
-__host__ __device__ inline int route_lds_ints(int E)
-{
-    int a = kRouteWaves * E;
-    int b = kRouteThreads + E + 1;
-    return a > b ? a : b;
-}
+// LDS ints k_route_rank needs for E experts.
+__host__ __device__ inline int route_lds_ints(int E) { return kRouteWaves * E + E + 1; }
 
 // Exclusive prefix sum over the block (kRouteThreads threads, one value each).
 __device__ inline int block_exclusive_sum(int v, int *wave_tot /* kRouteWaves+1 */, int *total)
@@ -126,18 +127,43 @@ __device__ inline int block_exclusive_sum(int v, int *wave_tot /* kRouteWaves+1 
     return wave_tot[wave] + incl - v;
 }
 
-__global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a)
+// expert_off from the expert totals (thread e < E holds total e), plus
+// rank_off / recv_count.  eoff: LDS [E+1].
+__device__ inline void write_offsets(const RouteArgs &a, int col_total, int *eoff, int *wave_tot)
+{
+    const int tid = threadIdx.x, E = a.num_experts;
+    int total;
+    const int excl = block_exclusive_sum(col_total, wave_tot, &total);
+    if (tid < E) {
+        eoff[tid] = excl;
+        a.expert_off[tid] = excl;
+    }
+    if (tid == 0) {
+        eoff[E] = total;
+        a.expert_off[E] = total;
+    }
+    __syncthreads();
+    const int R = a.num_ranks;
+    const int per_rank = E / R;
+    if (tid <= R)
+        a.rank_off[tid] = eoff[tid * per_rank];
+    if (tid < R)
+        a.recv_count[tid] = eoff[(tid + 1) * per_rank] - eoff[tid * per_rank];
+}
+
+template <bool SINGLE_TILE>
+__global__ __launch_bounds__(kRouteThreads) void k_route_rank(RouteArgs a)
 {
     extern __shared__ int32_t lds[];
     __shared__ int32_t s_wave_tot[kRouteWaves + 1];
-    __shared__ int32_t s_last;
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int E = a.num_experts;
     const int tile = blockIdx.x;
     const int p = tile * kRouteTile + tid;
-    int32_t *wave_cnt = lds;  // [kRouteWaves][E]
+    int32_t *wave_cnt = lds;                     // [kRouteWaves][E]
+    int32_t *eoff = lds + kRouteWaves * E;       // [E+1] (single tile)
 
     for (int i = tid; i < kRouteWaves * E; i += kRouteThreads)
         wave_cnt[i] = 0;
@@ -166,96 +192,106 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a)
         wave_cnt[wave * E + e] = __popcll(match);
     __syncthreads();
 
-    // per expert: exclusive prefix over the waves, and the tile total
+    // per expert: exclusive prefix over the waves (independent LDS loads
+    // first), and the tile total
+    int col_total = 0;
     for (int x = tid; x < E; x += kRouteThreads) {
+        int c[kRouteWaves];
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w)
+            c[w] = wave_cnt[w * E + x];
         int run = 0;
+#pragma unroll
         for (int w = 0; w < kRouteWaves; ++w) {
-            const int c = wave_cnt[w * E + x];
             wave_cnt[w * E + x] = run;
-            run += c;
+            run += c[w];
         }
-        a.tile_table[(size_t)tile * E + x] = run;
+        col_total = run;  // E <= kRouteThreads: one x per thread
+        if (!SINGLE_TILE)
+            a.tile_table[(size_t)tile * E + x] = run;
     }
     __syncthreads();
     if (p < a.n_pairs)
         a.rank_in_tile[p] = valid ? wave_cnt[wave * E + e] + rank_in_wave : -1;
 
-    // Publish the tile; the last block to arrive does the scan.
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t ticket = atomicAdd(&a.ctrl[kCtrlTicket], 1u);
-        s_last = ticket == gridDim.x - 1;
-        __threadfence();
+    if (SINGLE_TILE) {
+        // the only tile: its histogram is the whole histogram
+        write_offsets(a, col_total, eoff, s_wave_tot);
+        if (tid < E)
+            a.tile_table[tid] = eoff[tid];
     }
-    __syncthreads();
-    if (!s_last)
-        return;
-    __threadfence();
+}
 
-    const int B = gridDim.x;
+// One block.  Column chunks of up to kScanRegs tiles stay in registers
+// between the two passes; longer columns are re-read from memory.
+constexpr int kScanRegs = 16;
+
+__global__ __launch_bounds__(kRouteThreads) void k_route_scan(RouteArgs a)
+{
+    __shared__ int32_t part[kRouteThreads];
+    __shared__ int32_t eoff[kMaxExperts + 1];
+    __shared__ int32_t s_wave_tot[kRouteWaves + 1];
+
+    const int tid = threadIdx.x;
+    const int E = a.num_experts;
+    const int B = a.tiles;
     int G = kRouteThreads / E;  // threads per expert column, >= 1 since E <= 512
     if (G > B)
         G = B;
     const int chunk = (B + G - 1) / G;
-    int32_t *part = lds;                   // [G][E], G*E <= kRouteThreads
-    int32_t *eoff = lds + kRouteThreads;   // [E+1]
+    const bool in_regs = chunk <= kScanRegs;
+    const int g = tid / E, col = tid - (tid / E) * E;
+    const int b0 = g * chunk;
+    const int b1 = min(B, b0 + chunk);
 
-    for (int x = tid; x < G * E; x += kRouteThreads) {
-        const int g = x / E, col = x - g * E;
-        const int b0 = g * chunk;
-        const int b1 = min(B, b0 + chunk);
+    int vals[kScanRegs];
+    if (tid < G * E) {
         int sum = 0;
-#pragma unroll 8
-        for (int b = b0; b < b1; ++b)
-            sum += a.tile_table[(size_t)b * E + col];
-        part[x] = sum;
+        if (in_regs) {
+#pragma unroll
+            for (int r = 0; r < kScanRegs; ++r)
+                vals[r] = (b0 + r < b1) ? a.tile_table[(size_t)(b0 + r) * E + col] : 0;
+#pragma unroll
+            for (int r = 0; r < kScanRegs; ++r)
+                sum += vals[r];
+        } else {
+            for (int b = b0; b < b1; ++b)
+                sum += a.tile_table[(size_t)b * E + col];
+        }
+        part[tid] = sum;
     }
     __syncthreads();
 
     int col_total = 0;
     if (tid < E) {
         int run = 0;
-        for (int g = 0; g < G; ++g) {
-            const int c = part[g * E + tid];
-            part[g * E + tid] = run;
+        for (int gg = 0; gg < G; ++gg) {
+            const int c = part[gg * E + tid];
+            part[gg * E + tid] = run;
             run += c;
         }
         col_total = run;
     }
-    int total;
-    const int excl = block_exclusive_sum(col_total, s_wave_tot, &total);
-    if (tid < E) {
-        eoff[tid] = excl;
-        a.expert_off[tid] = excl;
-    }
-    if (tid == 0) {
-        eoff[E] = total;
-        a.expert_off[E] = total;
-    }
-    __syncthreads();
+    write_offsets(a, col_total, eoff, s_wave_tot);
 
-    const int R = a.num_ranks;
-    const int per_rank = E / R;
-    if (tid <= R)
-        a.rank_off[tid] = eoff[tid * per_rank];
-    if (tid < R)
-        a.recv_count[tid] = eoff[(tid + 1) * per_rank] - eoff[tid * per_rank];
-
-    for (int x = tid; x < G * E; x += kRouteThreads) {
-        const int g = x / E, col = x - g * E;
-        const int b0 = g * chunk;
-        const int b1 = min(B, b0 + chunk);
-        int run = eoff[col] + part[x];
-        for (int b = b0; b < b1; ++b) {
-            const size_t i = (size_t)b * E + col;
-            const int c = a.tile_table[i];
-            a.tile_table[i] = run;
-            run += c;
+    if (tid < G * E) {
+        int run = eoff[col] + part[tid];
+        if (in_regs) {
+#pragma unroll
+            for (int r = 0; r < kScanRegs; ++r)
+                if (b0 + r < b1) {
+                    a.tile_table[(size_t)(b0 + r) * E + col] = run;
+                    run += vals[r];
+                }
+        } else {
+            for (int b = b0; b < b1; ++b) {
+                const size_t i = (size_t)b * E + col;
+                const int c = a.tile_table[i];
+                a.tile_table[i] = run;
+                run += c;
+            }
         }
     }
-    if (tid == 0)
-        a.ctrl[kCtrlTicket] = 0;  // re-armed for the next dispatch
 }
 
 // ---------------------------------------------------------------------------
@@ -342,7 +378,8 @@ __device__ inline void carry_small_rows(const ScatterArgs &a, int t, int slot, i
     }
 }
 
-// bf16 or raw rows: read once, write K times (16-byte nontemporal stores).
+// bf16 or raw rows: read once, write K times (16-byte stores; on gfx950 plain
+// stores stream to HBM faster than nontemporal ones for this pattern).
 template <int CH>
 __global__ __launch_bounds__(256) void k_scatter_copy(ScatterArgs a)
 {
@@ -362,7 +399,7 @@ __global__ __launch_bounds__(256) void k_scatter_copy(ScatterArgs a)
         for (int i = 0; i < CH; ++i) {
             const int j = base + lane + kWave * i;
             if (j < V)
-                v[i] = src[j];
+                v[i] = __builtin_nontemporal_load(src + j);
         }
         for (int k = 0; k < a.topk; ++k) {
             const int s = read_lane(slot, k);
@@ -373,7 +410,7 @@ __global__ __launch_bounds__(256) void k_scatter_copy(ScatterArgs a)
             for (int i = 0; i < CH; ++i) {
                 const int j = base + lane + kWave * i;
                 if (j < V)
-                    __builtin_nontemporal_store(v[i], dst + j);
+                    dst[j] = v[i];
             }
         }
     }
@@ -401,7 +438,7 @@ __global__ __launch_bounds__(256) void k_scatter_fp8(ScatterArgs a)
             const int j = base + lane + kWave * i;
             u32x4 v = {0u, 0u, 0u, 0u};
             if (j < V)
-                v = src[j];
+                v = __builtin_nontemporal_load(src + j);
             float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                           bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
             float m = 0.0f;
@@ -435,7 +472,7 @@ __global__ __launch_bounds__(256) void k_scatter_fp8(ScatterArgs a)
             for (int i = 0; i < CH; ++i) {
                 const int j = base + lane + kWave * i;
                 if (j < V) {
-                    __builtin_nontemporal_store(code[i], dst + j);
+                    dst[j] = code[i];
                     if ((lane & 15) == 0)
                         dsc[j >> 4] = scale[i];
                 }
@@ -467,7 +504,7 @@ __global__ __launch_bounds__(256) void k_scatter_mxfp4(ScatterArgs a)
             const int j = base + lane + kWave * i;
             u32x4 v = {0u, 0u, 0u, 0u};
             if (j < V)
-                v = src[j];
+                v = __builtin_nontemporal_load(src + j);
             float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                           bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
             float m = 0.0f;
@@ -499,7 +536,7 @@ __global__ __launch_bounds__(256) void k_scatter_mxfp4(ScatterArgs a)
             for (int i = 0; i < CH; ++i) {
                 const int j = base + lane + kWave * i;
                 if (j < V) {
-                    __builtin_nontemporal_store(code[i], dst + j);
+                    dst[j] = code[i];
                     if ((lane & 3) == 0)
                         dsc[j >> 2] = (uint8_t)sbyte[i];
                 }
@@ -509,16 +546,26 @@ __global__ __launch_bounds__(256) void k_scatter_mxfp4(ScatterArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Combine: one wave per token, gather K rows, fp32 weighted sum, bf16 out
+// Combine: one wave per (token, row segment), K rows double buffered
 // ---------------------------------------------------------------------------
+//
+// A wave owns kCombineSeg 16-byte vectors per lane (a 2 KiB segment of a
+// bf16 row) of one token: it streams the segment of its K received rows in k
+// order, loading row k+1 while it accumulates row k, and writes the bf16
+// segment.  Splitting rows into segments gives several waves per token,
+// which measured faster than one wave walking the whole row.
+
+constexpr int kCombineSeg = 2;
+constexpr int kCombineSegVecs = kWave * kCombineSeg;
 
 struct CombineArgs {
     int32_t num_tokens;
     int32_t topk;
     int32_t row_vecs;        // 16-byte vectors per bf16 row (H/8)
+    int32_t segs;            // ceil(row_vecs / kCombineSegVecs)
     const int32_t *slot_of;  // [T*K]
-    const uint8_t *input;    // [N_cap, H] bf16
-    const float *weights;    // [N_cap, K] or NULL
+    const uint8_t *input;    // [rows, H] bf16
+    const float *weights;    // [rows, K] or NULL
     uint8_t *output;         // [T, H] bf16
     float *out_weights;      // [T, K] or NULL
 };
@@ -529,16 +576,32 @@ __device__ inline uint32_t pack_bf16_rne(float lo, float hi)
     return __builtin_bit_cast(uint32_t, b);
 }
 
-// KT = K (compile time) or kMaxTopk with the runtime K as bound.
-template <int KT, int CH>
-__global__ __launch_bounds__(256) void k_combine(CombineArgs a)
+__device__ inline void accumulate_row(float *acc, float w, u32x4 x)
 {
 #pragma clang fp contract(off)
+    acc[0] = acc[0] + w * bf16_lo(x.x);
+    acc[1] = acc[1] + w * bf16_hi(x.x);
+    acc[2] = acc[2] + w * bf16_lo(x.y);
+    acc[3] = acc[3] + w * bf16_hi(x.y);
+    acc[4] = acc[4] + w * bf16_lo(x.z);
+    acc[5] = acc[5] + w * bf16_hi(x.z);
+    acc[6] = acc[6] + w * bf16_lo(x.w);
+    acc[7] = acc[7] + w * bf16_hi(x.w);
+}
+
+// KT = K known at compile time (double-buffered), or 0: runtime K <= kMaxTopk.
+template <int KT>
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a)
+{
+    constexpr int CH = kCombineSeg;
     const int lane = threadIdx.x & (kWave - 1);
-    const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    if (t >= a.num_tokens)
+    const int wv = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (wv >= a.num_tokens * a.segs)
         return;
-    const int K = a.topk;
+    const int t = wv / a.segs;
+    const int sg = wv - t * a.segs;
+    const int K = KT > 0 ? KT : a.topk;
+
     int my_slot = -1;
     float my_w = 0.0f;
     if (lane < K) {
@@ -546,61 +609,82 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
         my_slot = a.slot_of[p];
         if (my_slot >= 0)
             my_w = a.weights ? a.weights[(size_t)my_slot * K + lane] : 1.0f;
-        if (a.out_weights)
+        if (a.out_weights && sg == 0)
             a.out_weights[p] = my_w;
     }
-    int slot[KT];
-    float w[KT];
-#pragma unroll
-    for (int k = 0; k < KT; ++k) {
-        slot[k] = (k < K) ? read_lane(my_slot, k) : -1;
-        w[k] = (k < K) ? read_lane_f(my_w, k) : 0.0f;
-    }
-
+    // the token's first slot: a safe row to load for pairs that have none
+    const uint64_t have = __ballot(my_slot >= 0);
     const int V = a.row_vecs;
-    const u32x4 *in = reinterpret_cast<const u32x4 *>(a.input);
+    const int base = sg * kCombineSegVecs;
     u32x4 *out = reinterpret_cast<u32x4 *>(a.output) + (size_t)t * V;
-    for (int base = 0; base < V; base += kWave * CH) {
-        u32x4 v[KT][CH];
-#pragma unroll
-        for (int k = 0; k < KT; ++k) {
-#pragma unroll
-            for (int i = 0; i < CH; ++i) {
-                const int j = base + lane + kWave * i;
-                if (slot[k] >= 0 && j < V)
-                    v[k][i] = in[(size_t)slot[k] * V + j];
-                else
-                    v[k][i] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
+    if (have == 0) {  // no pair of this token has a row: the sum is +0
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            float acc[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                acc[q] = 0.0f;
-#pragma unroll
-            for (int k = 0; k < KT; ++k) {
-                if (slot[k] < 0)
-                    continue;
-                const float wk = w[k];
-                const u32x4 x = v[k][i];
-                acc[0] = acc[0] + wk * bf16_lo(x.x);
-                acc[1] = acc[1] + wk * bf16_hi(x.x);
-                acc[2] = acc[2] + wk * bf16_lo(x.y);
-                acc[3] = acc[3] + wk * bf16_hi(x.y);
-                acc[4] = acc[4] + wk * bf16_lo(x.z);
-                acc[5] = acc[5] + wk * bf16_hi(x.z);
-                acc[6] = acc[6] + wk * bf16_lo(x.w);
-                acc[7] = acc[7] + wk * bf16_hi(x.w);
-            }
             const int j = base + lane + kWave * i;
-            if (j < V) {
-                const u32x4 r = {pack_bf16_rne(acc[0], acc[1]), pack_bf16_rne(acc[2], acc[3]),
-                                 pack_bf16_rne(acc[4], acc[5]), pack_bf16_rne(acc[6], acc[7])};
-                out[j] = r;
+            if (j < V)
+                out[j] = u32x4{0u, 0u, 0u, 0u};
+        }
+        return;
+    }
+    const int fallback = read_lane(my_slot, __builtin_ctzll(have));
+
+    const u32x4 *in = reinterpret_cast<const u32x4 *>(a.input);
+    float acc[CH][8];
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            acc[i][q] = 0.0f;
+
+    auto load_row = [&](int s, u32x4 *dst) {
+        const u32x4 *row = in + (size_t)s * V;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int j = base + lane + kWave * i;
+            dst[i] = j < V ? __builtin_nontemporal_load(row + j) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+
+    if constexpr (KT > 0) {
+        int slot[KT];
+        float w[KT];
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            slot[k] = read_lane(my_slot, k);
+            w[k] = read_lane_f(my_w, k);
+        }
+        u32x4 buf[2][CH];
+        load_row(slot[0] >= 0 ? slot[0] : fallback, buf[0]);
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            if (k + 1 < KT)
+                load_row(slot[k + 1] >= 0 ? slot[k + 1] : fallback, buf[(k + 1) & 1]);
+            if (slot[k] >= 0) {
+#pragma unroll
+                for (int i = 0; i < CH; ++i)
+                    accumulate_row(acc[i], w[k], buf[k & 1][i]);
             }
         }
+    } else {
+        for (int k = 0; k < K; ++k) {
+            const int s = read_lane(my_slot, k);
+            if (s < 0)
+                continue;
+            const float wk = read_lane_f(my_w, k);
+            u32x4 buf[CH];
+            load_row(s, buf);
+#pragma unroll
+            for (int i = 0; i < CH; ++i)
+                accumulate_row(acc[i], wk, buf[i]);
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int j = base + lane + kWave * i;
+        if (j < V)
+            out[j] = u32x4{pack_bf16_rne(acc[i][0], acc[i][1]), pack_bf16_rne(acc[i][2], acc[i][3]),
+                           pack_bf16_rne(acc[i][4], acc[i][5]), pack_bf16_rne(acc[i][6], acc[i][7])};
     }
 }
 

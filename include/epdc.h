@@ -102,12 +102,14 @@ typedef struct epdc_op epdc_op;
 
 /* Kernel ids for the profiling calls below. */
 enum {
-    EPDC_KERNEL_ROUTE = 0,         /* histogram + scan + in-tile ranks */
-    EPDC_KERNEL_SCATTER = 1,       /* slot + row copy (bf16 or raw) */
-    EPDC_KERNEL_SCATTER_FP8 = 2,   /* slot + E4M3 quantize + copy */
-    EPDC_KERNEL_SCATTER_MXFP4 = 3, /* slot + MXFP4 quantize + copy */
-    EPDC_KERNEL_COMBINE = 4,       /* gather + weighted fp32 sum */
-    EPDC_NUM_KERNELS = 5
+    EPDC_KERNEL_ROUTE = 0,         /* per-tile histograms + stable in-tile ranks
+                                      (and the scan, when there is one tile) */
+    EPDC_KERNEL_ROUTE_SCAN = 1,    /* scan to expert/rank offsets + tile bases */
+    EPDC_KERNEL_SCATTER = 2,       /* slot + row copy (bf16 or raw) */
+    EPDC_KERNEL_SCATTER_FP8 = 3,   /* slot + E4M3 quantize + copy */
+    EPDC_KERNEL_SCATTER_MXFP4 = 4, /* slot + MXFP4 quantize + copy */
+    EPDC_KERNEL_COMBINE = 5,       /* gather + weighted fp32 sum */
+    EPDC_NUM_KERNELS = 6
 };
 
 /* Bytes of device workspace an op with this config needs (host only, no GPU

@@ -105,8 +105,8 @@ def test_null_op_and_state_errors(lib):
 
 def test_kernel_names(lib):
     names = [B.epdc_kernel_name(k) for k in range(B.EPDC_NUM_KERNELS)]
-    assert names == ["k_route", "k_scatter_copy", "k_scatter_fp8", "k_scatter_mxfp4",
-                     "k_combine"]
+    assert names == ["k_route_rank", "k_route_scan", "k_scatter_copy", "k_scatter_fp8",
+                     "k_scatter_mxfp4", "k_combine"]
     assert B.epdc_kernel_name(B.EPDC_NUM_KERNELS) is None
 
 

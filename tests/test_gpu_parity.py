@@ -369,6 +369,6 @@ def test_profile_events_time_every_kernel():
         out, out_w, _, out_idx, _ = op.dispatch(x, wt, None, idx)
         op.combine(out, out_w, out_idx)
     prof = op.profile_end()
-    assert set(prof) == {"k_route", "k_scatter_copy", "k_combine"}
+    assert set(prof) == {"k_route_rank", "k_route_scan", "k_scatter_copy", "k_combine"}
     for name, (ms, n) in prof.items():
         assert n == 3 and ms > 0, name
