@@ -2,10 +2,11 @@
 
 One step = one dispatch (routing histogram, scan, stable slots, scatter of the
 bf16 rows with their weights/indices) followed by one combine (gather + fp32
-weighted top-k sum) of the dispatched rows (identity experts), on the
-DeepSeek-V3-shaped workload: 4096 tokens x hidden 7168, top-8 of 256 experts
-(Zipf 1.1 routing), 8 virtual ranks.  Inputs are resident in HBM before the
-timed region.  Prints one JSON line.
+weighted top-k sum) of the dispatched rows (identity experts), by default on
+the DeepSeek-V3-shaped workload: 4096 tokens x hidden 7168, top-8 of 256
+experts (Zipf 1.1 routing), 8 virtual ranks.  --workload picks another one
+(the quantizing workloads combine an independent bf16 expert output).
+Inputs are resident in HBM before the timed region.  Prints one JSON line.
 
 value = tokens/s of whole steps.  roofline: the kernel with the most time,
 algorithmic bytes per launch / its mean duration from HIP events recorded on
@@ -16,7 +17,6 @@ its last step is also compared bit for bit with the GPU's last timed step.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -27,7 +27,6 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published figure
-KERNEL_SRC = os.path.join(ROOT, "combine_routing_histogram_amd", "csrc", "epdc_kernels.hpp")
 
 
 def alg_bytes(kernel: str, w) -> int:
@@ -59,7 +58,8 @@ def alg_bytes(kernel: str, w) -> int:
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    from combine_routing_histogram_amd.profiling import kernel_source_hash as h
+    return h()
 
 
 def load_traffic(kernel: str, workload: str):
@@ -74,23 +74,30 @@ def load_traffic(kernel: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, inp, budget_s: float, gpu_payload, gpu_combined):
+def cpu_baseline(w, inp, budget_s: float, gpu_payload, gpu_scales, gpu_combined):
     """Time the oracle (plain C, one thread) on whole steps of the workload,
-    and compare its last step with the GPU's last timed step."""
+    and compare its last step with the GPU's last timed step (payload bytes,
+    produced scales, combine output)."""
     import numpy as np
 
     from oracle import oracle  # test infrastructure, used only by this leg
 
+    identity = w.combine_input == "identity"
     reps, t0 = 0, time.perf_counter()
     while True:
-        d = oracle.dispatch(inp["x"], inp["weights"], inp["indices"], w.experts, w.ranks)
-        y, _ = oracle.combine(d["out"], d["out_weights"], d["slot_of"], w.tokens, w.topk)
+        d = oracle.dispatch(inp["x"], inp["weights"], inp["indices"], w.experts, w.ranks,
+                            quant=w.quant)
+        c_in = d["out"] if identity else inp["combine_input"]
+        y, _ = oracle.combine(c_in, d["out_weights"], d["slot_of"], w.tokens, w.topk)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 50:
             break
     n = d["n_valid"]
-    same = (np.array_equal(gpu_payload[:n], d["out"]) and np.array_equal(gpu_combined, y))
+    same = (np.array_equal(gpu_payload[:n], d["out"].view(np.uint8).reshape(n, -1))
+            and np.array_equal(gpu_combined, y))
+    if d["out_scales"] is not None:
+        same = same and np.array_equal(gpu_scales[:n], d["out_scales"].view(np.uint8).reshape(n, -1))
     base = {"value": w.tokens * reps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} whole dispatch+combine steps of {w.name} "
                       f"({w.tokens} tokens each), {el:.1f} s"}
@@ -103,9 +110,14 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="deepseek_v3_bf16")
-    ap.add_argument("--kernel-events", choices=["timed", "separate"], default="timed",
-                    help="record the per-kernel events in the timed steps, or in a second "
-                         "pass of the same number of steps")
+    ap.add_argument("--kernel-events", choices=["timed", "separate"], default="separate",
+                    help="record the per-kernel events in the timed steps, or (default) in a "
+                         "second pass of the same number of steps right after them: each "
+                         "event record costs about 3.5 us of GPU time, which would inflate "
+                         "the step time")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the steps "
+                         "(a known-size kernel for scaling rocprofv3 byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU-oracle baseline (0 = skip)")
     args = ap.parse_args()
@@ -123,24 +135,34 @@ def main() -> int:
     from combine_routing_histogram_amd.op import EpDispatchCombineConfig, EpDispatchCombineOp
 
     w = wl.WORKLOADS[args.workload]
-    if w.quant != "none" or w.combine_input != "identity":
-        print("bench.py times the identity-expert bf16 workloads", file=sys.stderr)
-        return 2
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     print(f"bench: {w.name} T={w.tokens} H={w.hidden} K={w.topk} E={w.experts} R={w.ranks}",
           file=sys.stderr, flush=True)
 
+    def to_bf16(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
     inp = wl.make_inputs(w)
-    x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    x = to_bf16(inp["x"])
     idx = torch.from_numpy(inp["indices"]).to(dev)
     wts = torch.from_numpy(inp["weights"]).to(dev)
+    identity = w.combine_input == "identity"
+    c_in = None if identity else to_bf16(inp["combine_input"])
     op = EpDispatchCombineOp(EpDispatchCombineConfig(w.tokens, w.hidden, w.topk, w.experts,
-                                                     w.ranks), dev)
+                                                     w.ranks, quant=w.quant), dev)
 
     def step():
         out, out_w, _, out_idx, _ = op.dispatch(x, wts, None, idx)
-        return op.combine(out, out_w, out_idx)
+        return op.combine(out if identity else c_in, out_w, out_idx)
+
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -183,11 +205,15 @@ def main() -> int:
     # the method's bytes: x read once, K row copies written, K rows read back, one row
     # written, plus the small per-pair arrays (the route's own index read and rank array
     # are workspace traffic, not counted)
-    step_bytes = alg_bytes("k_scatter_copy", w) + alg_bytes("k_combine", w)
+    scatter_name = {"none": "k_scatter_copy", "fp8_e4m3_b128": "k_scatter_fp8",
+                    "mxfp4_b32": "k_scatter_mxfp4"}[w.quant]
+    step_bytes = alg_bytes(scatter_name, w) + alg_bytes("k_combine", w)
     traffic = load_traffic(dom, w.name)
 
     result = {
-        "metric": "dispatch+combine tokens/s and achieved HBM GB/s (% peak), 4096x7168 top-8",
+        "metric": "dispatch+combine tokens/s and achieved HBM GB/s (% peak), 4096x7168 top-8"
+                  if w.name == "deepseek_v3_bf16" else
+                  f"dispatch+combine tokens/s and achieved HBM GB/s (% peak), {w.name}",
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -197,11 +223,14 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": {"none": "bf16", "fp8_e4m3_b128": "bf16->e4m3 (fp32 scales), fp32 combine",
+                  "mxfp4_b32": "bf16->e2m1 (e8m0 scales), fp32 combine"}[w.quant],
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.tokens, "hidden": w.hidden, "topk": w.topk,
                    "experts": w.experts, "ranks": w.ranks, "routing": f"{w.routing}{w.zipf_s or ''}",
-                   "quant": w.quant, "combine_input": "identity (dispatch output)",
+                   "quant": w.quant,
+                   "combine_input": "identity (dispatch output)" if identity
+                   else "independent N(0,1) bf16 rows",
                    "graph_mode": "eager", "gpu": torch.cuda.get_device_name(dev)},
         "step_alg_bytes": step_bytes,
         "step_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
@@ -216,9 +245,12 @@ def main() -> int:
     parity = "skipped"
     result["cpu_baseline"] = None
     if args.cpu_seconds > 0:
-        payload = op.received_payload().view(torch.int16).cpu().numpy().view(np.uint16)
+        payload = op.received_payload().view(torch.uint8).cpu().numpy()
+        scales = op.received_scales(False)
+        scales = None if scales is None else scales.view(torch.uint8).cpu().numpy()
         combined = y.view(torch.int16).cpu().numpy().view(np.uint16)
-        result["cpu_baseline"], parity = cpu_baseline(w, inp, args.cpu_seconds, payload, combined)
+        result["cpu_baseline"], parity = cpu_baseline(w, inp, args.cpu_seconds, payload, scales,
+                                                      combined)
     result["parity"] = parity
     print(json.dumps(result), flush=True)
     return 0 if parity != "MISMATCH" else 1

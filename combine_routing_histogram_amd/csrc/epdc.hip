@@ -186,9 +186,56 @@ epdc_status launch(epdc_op *op, hipStream_t st, int kernel_id, F &&f)
     return EPDC_SUCCESS;
 }
 
-// One wave per token; bigger blocks once there are enough tokens to fill the
-// chip with them.
-int waves_per_block(int tokens) { return tokens >= 2048 ? 4 : 1; }
+// How a scatter launch splits token rows: CH 16-byte vectors per lane per
+// pass, segments of seg_vecs vectors (a multiple of 64*CH), one wave each.
+struct ScatterPlan {
+    int ch, seg_vecs, segs;
+};
+
+ScatterPlan make_plan(int ch, int row_vecs, int max_segs)
+{
+    const int pass = kWave * ch;
+    const int passes = (row_vecs + pass - 1) / pass;
+    int segs = max_segs < passes ? max_segs : passes;
+    if (segs < 1)
+        segs = 1;
+    const int per_seg = (passes + segs - 1) / segs;
+    ScatterPlan p;
+    p.ch = ch;
+    p.seg_vecs = per_seg * pass;
+    p.segs = (passes + per_seg - 1) / per_seg;
+    return p;
+}
+
+// Measured on MI355X in the dispatch -> combine loop (see the design notes):
+// the bf16 copy streams best with one wave per token once there are enough
+// tokens to fill the chip; the quantizing kernels and small batches need more,
+// shorter waves per token to hide their per-wave latency.
+ScatterPlan plan_scatter(int quant, int tokens, int row_vecs)
+{
+    switch (quant) {
+    case EPDC_QUANT_FP8_E4M3_B128:
+        return make_plan(1, row_vecs, 1 << 20);
+    case EPDC_QUANT_MXFP4_B32:
+        return make_plan(2, row_vecs, 1 << 20);
+    default:
+        return tokens >= 2048 ? make_plan(8, row_vecs, 1) : make_plan(2, row_vecs, 1 << 20);
+    }
+}
+
+// Grid of one-wave work items: 4 waves per block once there are enough waves
+// to fill the chip with such blocks, else single-wave blocks spread over more
+// CUs.
+epdc_status grid_for_waves(int64_t waves, int *grid, int *block)
+{
+    if (waves <= 0 || waves > (int64_t)0x7FFFFFFF - 4)
+        return fail(EPDC_ERR_INVALID_ARGS, "work of %lld waves does not fit one launch",
+                    (long long)waves);
+    const int wpb = waves >= 4096 ? 4 : 1;
+    *grid = (int)((waves + wpb - 1) / wpb);
+    *block = wpb * kWave;
+    return EPDC_SUCCESS;
+}
 
 template <int KT>
 void launch_combine(int grid, int block, hipStream_t st, const CombineArgs &a)
@@ -382,21 +429,38 @@ epdc_status epdc_dispatch(epdc_op *op, void *stream, int32_t num_tokens, const v
     sa.scale_words = c.scale_row_bytes / 4;
     sa.ctrl = op->ctrl();
 
-    const int wpb = waves_per_block(num_tokens);
-    const int grid = (num_tokens + wpb - 1) / wpb;
-    const int block = wpb * kWave;
+    const int in_vecs = c.quant == EPDC_QUANT_NONE ? sa.in_row_vecs : c.hidden / 8;
+    const ScatterPlan plan = plan_scatter(c.quant, num_tokens, in_vecs);
+    sa.segs = plan.segs;
+    sa.seg_vecs = plan.seg_vecs;
+    int grid, block;
+    s = grid_for_waves((int64_t)num_tokens * sa.segs, &grid, &block);
+    if (s != EPDC_SUCCESS)
+        return s;
     switch (c.quant) {
     case EPDC_QUANT_FP8_E4M3_B128:
-        s = launch(op, st, EPDC_KERNEL_SCATTER_FP8,
-                   [&] { k_scatter_fp8<4><<<grid, block, 0, st>>>(sa); });
+        s = launch(op, st, EPDC_KERNEL_SCATTER_FP8, [&] {
+            if (plan.ch == 1)
+                k_scatter_fp8<1><<<grid, block, 0, st>>>(sa);
+            else
+                k_scatter_fp8<2><<<grid, block, 0, st>>>(sa);
+        });
         break;
     case EPDC_QUANT_MXFP4_B32:
-        s = launch(op, st, EPDC_KERNEL_SCATTER_MXFP4,
-                   [&] { k_scatter_mxfp4<4><<<grid, block, 0, st>>>(sa); });
+        s = launch(op, st, EPDC_KERNEL_SCATTER_MXFP4, [&] {
+            if (plan.ch == 1)
+                k_scatter_mxfp4<1><<<grid, block, 0, st>>>(sa);
+            else
+                k_scatter_mxfp4<2><<<grid, block, 0, st>>>(sa);
+        });
         break;
     default:
-        s = launch(op, st, EPDC_KERNEL_SCATTER,
-                   [&] { k_scatter_copy<8><<<grid, block, 0, st>>>(sa); });
+        s = launch(op, st, EPDC_KERNEL_SCATTER, [&] {
+            if (plan.ch == 8)
+                k_scatter_copy<8><<<grid, block, 0, st>>>(sa);
+            else
+                k_scatter_copy<2><<<grid, block, 0, st>>>(sa);
+        });
         break;
     }
     if (s != EPDC_SUCCESS)
@@ -435,11 +499,11 @@ epdc_status epdc_combine(epdc_op *op, void *stream, const void *input, const flo
     ca.out_weights = out_weights;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int waves = T * ca.segs;  // one wave per (token, row segment)
-    const int wpb = waves >= 4096 ? 4 : 1;
-    const int grid = (waves + wpb - 1) / wpb;
-    const int block = wpb * kWave;
-    epdc_status s = launch(op, st, EPDC_KERNEL_COMBINE, [&] {
+    int grid, block;  // one wave per (token, row segment)
+    epdc_status s = grid_for_waves((int64_t)T * ca.segs, &grid, &block);
+    if (s != EPDC_SUCCESS)
+        return s;
+    s = launch(op, st, EPDC_KERNEL_COMBINE, [&] {
         switch (c.topk) {
         case 1: launch_combine<1>(grid, block, st, ca); break;
         case 2: launch_combine<2>(grid, block, st, ca); break;

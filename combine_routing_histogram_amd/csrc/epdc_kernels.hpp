@@ -295,8 +295,16 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scan(RouteArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// Dispatch scatter: one wave per token
+// Dispatch scatter: one wave per (token, row segment)
 // ---------------------------------------------------------------------------
+//
+// A wave owns a segment of one token row (seg_vecs 16-byte input vectors,
+// CH per lane per pass): it reads each vector once, quantizes it if asked,
+// and writes it to the token's K received rows.  Several waves per token keep the grid
+// many waves deep, so the kernel is bound by HBM throughput rather than by
+// the latency of one wave walking a whole row.  Every wave of a token derives
+// the same K slots; the wave of segment 0 records them and carries the small
+// per-slot rows (weights, indices, scales).
 
 struct ScatterArgs {
     int32_t num_tokens;
@@ -304,6 +312,8 @@ struct ScatterArgs {
     int32_t topk;
     int32_t num_experts;
     int32_t hidden;              // bf16 elements per row (quantizing kernels)
+    int32_t segs;                // row segments per token
+    int32_t seg_vecs;            // input vectors per segment (a multiple of 64*CH)
     const int32_t *indices;      // [T, K]
     const int32_t *tile_table;   // first slot per (tile, expert)
     const int32_t *rank_in_tile; // [T*K]
@@ -321,8 +331,8 @@ struct ScatterArgs {
     uint32_t *ctrl;              // error flag
 };
 
-// Slot of this lane's pair (lanes < K), also recorded in slot_of / src_pos.
-__device__ inline int pair_slot(const ScatterArgs &a, int t, int lane)
+// Slot of this lane's pair (lanes < K); `record` also stores slot_of / src_pos.
+__device__ inline int pair_slot(const ScatterArgs &a, int t, int lane, bool record)
 {
     int s = -1;
     if (lane < a.topk) {
@@ -331,15 +341,17 @@ __device__ inline int pair_slot(const ScatterArgs &a, int t, int lane)
         if (r >= 0) {
             const int e = a.indices[p];
             s = a.tile_table[(size_t)(p / kRouteTile) * a.num_experts + e] + r;
-            if ((unsigned)s < (unsigned)a.n_pairs) {
-                a.src_pos[s] = p;
-            } else {
+            if ((unsigned)s >= (unsigned)a.n_pairs) {
                 // cannot happen for a consistent routing table; never write out of bounds
-                atomicOr(&a.ctrl[kCtrlError], 2u);
+                if (record)
+                    atomicOr(&a.ctrl[kCtrlError], 2u);
                 s = -1;
+            } else if (record) {
+                a.src_pos[s] = p;
             }
         }
-        a.slot_of[p] = s;
+        if (record)
+            a.slot_of[p] = s;
     }
     return s;
 }
@@ -378,38 +390,56 @@ __device__ inline void carry_small_rows(const ScatterArgs &a, int t, int slot, i
     }
 }
 
-// bf16 or raw rows: read once, write K times (16-byte stores; on gfx950 plain
-// stores stream to HBM faster than nontemporal ones for this pattern).
+// Token, segment and K slots of this wave; false if the wave has no work.
+struct ScatterWave {
+    int lane, t, base, end, slot;
+};
+
+__device__ inline bool scatter_wave(const ScatterArgs &a, int row_vecs, ScatterWave &w)
+{
+    w.lane = threadIdx.x & (kWave - 1);
+    const int wv = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (wv >= a.num_tokens * a.segs)
+        return false;
+    w.t = wv / a.segs;
+    const int sg = wv - w.t * a.segs;
+    w.base = sg * a.seg_vecs;
+    w.end = min(row_vecs, w.base + a.seg_vecs);
+    w.slot = pair_slot(a, w.t, w.lane, sg == 0);
+    if (sg == 0)
+        carry_small_rows(a, w.t, w.slot, w.lane);
+    return true;
+}
+
+// bf16 or raw rows: 16-byte nontemporal loads once, K rows of ordinary 16-byte
+// stores (on gfx950 ordinary stores stream this 1->K pattern to HBM faster
+// than nontemporal ones).
 template <int CH>
 __global__ __launch_bounds__(256) void k_scatter_copy(ScatterArgs a)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    if (t >= a.num_tokens)
-        return;
-    const int slot = pair_slot(a, t, lane);
-    carry_small_rows(a, t, slot, lane);
-
     const int V = a.in_row_vecs;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)t * V;
+    ScatterWave w;
+    if (!scatter_wave(a, V, w))
+        return;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)w.t * V;
     u32x4 *out = reinterpret_cast<u32x4 *>(a.out);
-    for (int base = 0; base < V; base += kWave * CH) {
+    for (int b = w.base; b < w.end; b += kWave * CH) {
         u32x4 v[CH];
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            const int j = base + lane + kWave * i;
-            if (j < V)
+            const int j = b + w.lane + kWave * i;
+            if (j < w.end)
                 v[i] = __builtin_nontemporal_load(src + j);
         }
         for (int k = 0; k < a.topk; ++k) {
-            const int s = read_lane(slot, k);
+            const int s = read_lane(w.slot, k);
             if (s < 0)
                 continue;
             u32x4 *dst = out + (size_t)s * V;
 #pragma unroll
             for (int i = 0; i < CH; ++i) {
-                const int j = base + lane + kWave * i;
-                if (j < V)
+                const int j = b + w.lane + kWave * i;
+                if (j < w.end)
                     dst[j] = v[i];
             }
         }
@@ -417,67 +447,64 @@ __global__ __launch_bounds__(256) void k_scatter_copy(ScatterArgs a)
 }
 
 // OCP E4M3 with one fp32 scale per 128 elements (16 lanes x 8 elements).
+// Segments are whole numbers of 16-vector blocks.
 template <int CH>
 __global__ __launch_bounds__(256) void k_scatter_fp8(ScatterArgs a)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    if (t >= a.num_tokens)
-        return;
-    const int slot = pair_slot(a, t, lane);
-    carry_small_rows(a, t, slot, lane);
-
     const int V = a.hidden / 8;          // 8 bf16 per vector
     const int nblk = a.hidden / 128;     // scales per row
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)t * V;
-    for (int base = 0; base < V; base += kWave * CH) {
-        u32x2 code[CH];
-        float scale[CH];
+    ScatterWave w;
+    if (!scatter_wave(a, V, w))
+        return;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)w.t * V;
+    for (int b = w.base; b < w.end; b += kWave * CH) {
+    u32x2 code[CH];
+    float scale[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int j = b + w.lane + kWave * i;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (j < w.end)
+            v = __builtin_nontemporal_load(src + j);
+        float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                      bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        float m = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            m = fmaxf(m, fabsf(x[q]));
+        // V is a multiple of 16, so the 16 lanes of a block are all in or all out
+        m = fmaxf(m, __shfl_xor(m, 1, kWave));
+        m = fmaxf(m, __shfl_xor(m, 2, kWave));
+        m = fmaxf(m, __shfl_xor(m, 4, kWave));
+        m = fmaxf(m, __shfl_xor(m, 8, kWave));
+        float s = 0.0f;
+        uint32_t lo = 0, hi = 0;
+        if (m != 0.0f) {
+            s = m / 448.0f;  // IEEE division, round to nearest
+            lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] / s, x[1] / s, lo, false);
+            lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] / s, x[3] / s, lo, true);
+            hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] / s, x[5] / s, hi, false);
+            hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] / s, x[7] / s, hi, true);
+        }
+        code[i] = u32x2{lo, hi};
+        scale[i] = s;
+    }
+    for (int k = 0; k < a.topk; ++k) {
+        const int s = read_lane(w.slot, k);
+        if (s < 0)
+            continue;
+        u32x2 *dst = reinterpret_cast<u32x2 *>(a.out + (size_t)s * a.hidden);
+        float *dsc = reinterpret_cast<float *>(a.out_scales) + (size_t)s * nblk;
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            const int j = base + lane + kWave * i;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (j < V)
-                v = __builtin_nontemporal_load(src + j);
-            float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                          bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-            float m = 0.0f;
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                m = fmaxf(m, fabsf(x[q]));
-            // V is a multiple of 16, so the 16 lanes of a block are all in or all out
-            m = fmaxf(m, __shfl_xor(m, 1, kWave));
-            m = fmaxf(m, __shfl_xor(m, 2, kWave));
-            m = fmaxf(m, __shfl_xor(m, 4, kWave));
-            m = fmaxf(m, __shfl_xor(m, 8, kWave));
-            float s = 0.0f;
-            uint32_t lo = 0, hi = 0;
-            if (m != 0.0f) {
-                s = m / 448.0f;  // IEEE division, round to nearest
-                lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] / s, x[1] / s, lo, false);
-                lo = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] / s, x[3] / s, lo, true);
-                hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] / s, x[5] / s, hi, false);
-                hi = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] / s, x[7] / s, hi, true);
-            }
-            code[i] = u32x2{lo, hi};
-            scale[i] = s;
-        }
-        for (int k = 0; k < a.topk; ++k) {
-            const int s = read_lane(slot, k);
-            if (s < 0)
-                continue;
-            u32x2 *dst = reinterpret_cast<u32x2 *>(a.out + (size_t)s * a.hidden);
-            float *dsc = reinterpret_cast<float *>(a.out_scales) + (size_t)s * nblk;
-#pragma unroll
-            for (int i = 0; i < CH; ++i) {
-                const int j = base + lane + kWave * i;
-                if (j < V) {
-                    dst[j] = code[i];
-                    if ((lane & 15) == 0)
-                        dsc[j >> 4] = scale[i];
-                }
+            const int j = b + w.lane + kWave * i;
+            if (j < w.end) {
+                dst[j] = code[i];
+                if ((w.lane & 15) == 0)
+                    dsc[j >> 4] = scale[i];
             }
         }
+    }
     }
 }
 
@@ -486,62 +513,58 @@ __global__ __launch_bounds__(256) void k_scatter_fp8(ScatterArgs a)
 template <int CH>
 __global__ __launch_bounds__(256) void k_scatter_mxfp4(ScatterArgs a)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    if (t >= a.num_tokens)
-        return;
-    const int slot = pair_slot(a, t, lane);
-    carry_small_rows(a, t, slot, lane);
-
     const int V = a.hidden / 8;
     const int nblk = a.hidden / 32;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)t * V;
-    for (int base = 0; base < V; base += kWave * CH) {
-        uint32_t code[CH];
-        uint32_t sbyte[CH];
+    ScatterWave w;
+    if (!scatter_wave(a, V, w))
+        return;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)w.t * V;
+    for (int b = w.base; b < w.end; b += kWave * CH) {
+    uint32_t code[CH];
+    uint32_t sbyte[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int j = b + w.lane + kWave * i;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (j < w.end)
+            v = __builtin_nontemporal_load(src + j);
+        float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                      bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        float m = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            m = fmaxf(m, fabsf(x[q]));
+        m = fmaxf(m, __shfl_xor(m, 1, kWave));
+        m = fmaxf(m, __shfl_xor(m, 2, kWave));
+        // E8M0 byte = floor(log2 amax) - 2 + 127, clamped at 0: the fp32
+        // exponent field minus 2 (0 for zero or subnormal amax)
+        const uint32_t ef = (__float_as_uint(m) >> 23) & 0xFFu;
+        const uint32_t sb = ef > 2u ? ef - 2u : 0u;
+        const float scale = __uint_as_float(sb << 23);  // only its exponent field is used
+        uint32_t q = 0;
+        q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, x[0], x[1], scale, 0);
+        q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, x[2], x[3], scale, 1);
+        q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, x[4], x[5], scale, 2);
+        q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, x[6], x[7], scale, 3);
+        code[i] = q;
+        sbyte[i] = sb;
+    }
+    for (int k = 0; k < a.topk; ++k) {
+        const int s = read_lane(w.slot, k);
+        if (s < 0)
+            continue;
+        uint32_t *dst = reinterpret_cast<uint32_t *>(a.out + (size_t)s * (a.hidden / 2));
+        uint8_t *dsc = a.out_scales + (size_t)s * nblk;
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            const int j = base + lane + kWave * i;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (j < V)
-                v = __builtin_nontemporal_load(src + j);
-            float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                          bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-            float m = 0.0f;
-#pragma unroll
-            for (int q = 0; q < 8; ++q)
-                m = fmaxf(m, fabsf(x[q]));
-            m = fmaxf(m, __shfl_xor(m, 1, kWave));
-            m = fmaxf(m, __shfl_xor(m, 2, kWave));
-            // E8M0 byte = floor(log2 amax) - 2 + 127, clamped at 0: the fp32
-            // exponent field minus 2 (0 for zero or subnormal amax)
-            const uint32_t ef = (__float_as_uint(m) >> 23) & 0xFFu;
-            const uint32_t sb = ef > 2u ? ef - 2u : 0u;
-            const float scale = __uint_as_float(sb << 23);  // 2^(sb-127), exponent field only
-            uint32_t q = 0;
-            q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, x[0], x[1], scale, 0);
-            q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, x[2], x[3], scale, 1);
-            q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, x[4], x[5], scale, 2);
-            q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, x[6], x[7], scale, 3);
-            code[i] = q;
-            sbyte[i] = sb;
-        }
-        for (int k = 0; k < a.topk; ++k) {
-            const int s = read_lane(slot, k);
-            if (s < 0)
-                continue;
-            uint32_t *dst = reinterpret_cast<uint32_t *>(a.out + (size_t)s * (a.hidden / 2));
-            uint8_t *dsc = a.out_scales + (size_t)s * nblk;
-#pragma unroll
-            for (int i = 0; i < CH; ++i) {
-                const int j = base + lane + kWave * i;
-                if (j < V) {
-                    dst[j] = code[i];
-                    if ((lane & 3) == 0)
-                        dsc[j >> 2] = (uint8_t)sbyte[i];
-                }
+            const int j = b + w.lane + kWave * i;
+            if (j < w.end) {
+                dst[j] = code[i];
+                if ((w.lane & 3) == 0)
+                    dsc[j >> 2] = (uint8_t)sbyte[i];
             }
         }
+    }
     }
 }
 
