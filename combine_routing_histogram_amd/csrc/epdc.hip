@@ -9,6 +9,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -211,7 +212,7 @@ ScatterPlan make_plan(int ch, int row_vecs, int max_segs)
 // the bf16 copy streams best with one wave per token once there are enough
 // tokens to fill the chip; the quantizing kernels and small batches need more,
 // shorter waves per token to hide their per-wave latency.
-ScatterPlan plan_scatter(int quant, int tokens, int row_vecs)
+ScatterPlan plan_scatter(int quant, int tokens, int row_vecs, bool inline_route)
 {
     switch (quant) {
     case EPDC_QUANT_FP8_E4M3_B128:
@@ -219,7 +220,8 @@ ScatterPlan plan_scatter(int quant, int tokens, int row_vecs)
     case EPDC_QUANT_MXFP4_B32:
         return make_plan(2, row_vecs, 1 << 20);
     default:
-        return tokens >= 2048 ? make_plan(8, row_vecs, 1) : make_plan(2, row_vecs, 1 << 20);
+        return tokens >= 2048 && !inline_route ? make_plan(8, row_vecs, 1)
+                                               : make_plan(2, row_vecs, 1 << 20);
     }
 }
 
@@ -228,7 +230,7 @@ ScatterPlan plan_scatter(int quant, int tokens, int row_vecs)
 // CUs.
 epdc_status grid_for_waves(int64_t waves, int *grid, int *block)
 {
-    if (waves <= 0 || waves > (int64_t)0x7FFFFFFF - 4)
+    if (waves <= 0 || waves > (int64_t)0x7FFFFFFF - 64)
         return fail(EPDC_ERR_INVALID_ARGS, "work of %lld waves does not fit one launch",
                     (long long)waves);
     const int wpb = waves >= 4096 ? 4 : 1;
@@ -386,8 +388,12 @@ epdc_status epdc_dispatch(epdc_op *op, void *stream, int32_t num_tokens, const v
     ra.recv_count = recv_count;
     ra.ctrl = op->ctrl();
     const size_t lds = sizeof(int32_t) * (size_t)route_lds_ints(c.num_experts);
-    epdc_status s;
-    if (tiles == 1) {
+    // One tile with tokens: the scatter launch below routes by itself.
+    const bool inline_route = tiles == 1 && num_tokens > 0;
+    epdc_status s = EPDC_SUCCESS;
+    if (inline_route) {
+        // no route launch
+    } else if (tiles == 1) {
         s = launch(op, st, EPDC_KERNEL_ROUTE, [&] {
             k_route_rank<true><<<1, kRouteThreads, lds, st>>>(ra);
         });
@@ -428,35 +434,52 @@ epdc_status epdc_dispatch(epdc_op *op, void *stream, int32_t num_tokens, const v
     sa.out_scales = static_cast<uint8_t *>(out_scales);
     sa.scale_words = c.scale_row_bytes / 4;
     sa.ctrl = op->ctrl();
+    sa.key_bits = op->key_bits;
+    sa.num_ranks = c.num_ranks;
+    sa.expert_off = ra.expert_off;
+    sa.rank_off = ra.rank_off;
+    sa.recv_count = recv_count;
 
     const int in_vecs = c.quant == EPDC_QUANT_NONE ? sa.in_row_vecs : c.hidden / 8;
-    const ScatterPlan plan = plan_scatter(c.quant, num_tokens, in_vecs);
+    const ScatterPlan plan = plan_scatter(c.quant, num_tokens, in_vecs, inline_route);
     sa.segs = plan.segs;
     sa.seg_vecs = plan.seg_vecs;
     int grid, block;
-    s = grid_for_waves((int64_t)num_tokens * sa.segs, &grid, &block);
-    if (s != EPDC_SUCCESS)
-        return s;
+    const int64_t waves = (int64_t)num_tokens * sa.segs;
+    if (inline_route) {
+        // kRouteThreads threads per block for the ranking; about 256 blocks
+        // share the copies (waves <= 1024 * 64 here: at most one tile of pairs)
+        sa.work_waves = (int)std::min<int64_t>(kRouteWaves, std::max<int64_t>(1, (waves + 255) / 256));
+        grid = (int)((waves + sa.work_waves - 1) / sa.work_waves);
+        block = kRouteThreads;
+    } else {
+        s = grid_for_waves(waves, &grid, &block);
+        if (s != EPDC_SUCCESS)
+            return s;
+        sa.work_waves = block / kWave;
+    }
     switch (c.quant) {
     case EPDC_QUANT_FP8_E4M3_B128:
         s = launch(op, st, EPDC_KERNEL_SCATTER_FP8, [&] {
-            if (plan.ch == 1)
-                k_scatter_fp8<1><<<grid, block, 0, st>>>(sa);
+            if (inline_route)
+                k_scatter_fp8<1, true><<<grid, block, 0, st>>>(sa);
             else
-                k_scatter_fp8<2><<<grid, block, 0, st>>>(sa);
+                k_scatter_fp8<1><<<grid, block, 0, st>>>(sa);
         });
         break;
     case EPDC_QUANT_MXFP4_B32:
         s = launch(op, st, EPDC_KERNEL_SCATTER_MXFP4, [&] {
-            if (plan.ch == 1)
-                k_scatter_mxfp4<1><<<grid, block, 0, st>>>(sa);
+            if (inline_route)
+                k_scatter_mxfp4<2, true><<<grid, block, 0, st>>>(sa);
             else
                 k_scatter_mxfp4<2><<<grid, block, 0, st>>>(sa);
         });
         break;
     default:
         s = launch(op, st, EPDC_KERNEL_SCATTER, [&] {
-            if (plan.ch == 8)
+            if (inline_route)
+                k_scatter_copy<2, true><<<grid, block, 0, st>>>(sa);
+            else if (plan.ch == 8)
                 k_scatter_copy<8><<<grid, block, 0, st>>>(sa);
             else
                 k_scatter_copy<2><<<grid, block, 0, st>>>(sa);

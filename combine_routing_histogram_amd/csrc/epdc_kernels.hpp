@@ -128,59 +128,62 @@ __device__ inline int block_exclusive_sum(int v, int *wave_tot /* kRouteWaves+1 
 }
 
 // expert_off from the expert totals (thread e < E holds total e), plus
-// rank_off / recv_count.  eoff: LDS [E+1].
-__device__ inline void write_offsets(const RouteArgs &a, int col_total, int *eoff, int *wave_tot)
+// rank_off / recv_count; eoff: LDS [E+1] (filled in every block); only a
+// block with `publish` writes the global arrays.
+__device__ inline void write_offsets(int E, int R, int col_total, int *eoff, int *wave_tot,
+                                     int32_t *expert_off, int32_t *rank_off, int32_t *recv_count,
+                                     bool publish)
 {
-    const int tid = threadIdx.x, E = a.num_experts;
+    const int tid = threadIdx.x;
     int total;
     const int excl = block_exclusive_sum(col_total, wave_tot, &total);
-    if (tid < E) {
+    if (tid < E)
         eoff[tid] = excl;
-        a.expert_off[tid] = excl;
-    }
-    if (tid == 0) {
+    if (tid == 0)
         eoff[E] = total;
-        a.expert_off[E] = total;
-    }
     __syncthreads();
-    const int R = a.num_ranks;
+    if (!publish)
+        return;
+    if (tid <= E)
+        expert_off[tid] = eoff[tid];
     const int per_rank = E / R;
     if (tid <= R)
-        a.rank_off[tid] = eoff[tid * per_rank];
+        rank_off[tid] = eoff[tid * per_rank];
     if (tid < R)
-        a.recv_count[tid] = eoff[(tid + 1) * per_rank] - eoff[tid * per_rank];
+        recv_count[tid] = eoff[(tid + 1) * per_rank] - eoff[tid * per_rank];
 }
 
-template <bool SINGLE_TILE>
-__global__ __launch_bounds__(kRouteThreads) void k_route_rank(RouteArgs a)
-{
-    extern __shared__ int32_t lds[];
-    __shared__ int32_t s_wave_tot[kRouteWaves + 1];
+// Stable ranks of one tile of pairs, one pair per thread of a kRouteThreads
+// block.  Thread `tid` holds pair p (p >= n_pairs: no pair).  Returns its
+// expert (-1: none or an id outside [0, E), which raises the error flag when
+// `flag_errors`), its rank among the tile's pairs with the same expert, and
+// for threads x < E the tile's count of expert x.  wave_cnt: LDS
+// [kRouteWaves][E].
+struct TileRank {
+    int e, rank, col_total;
+};
 
+__device__ inline TileRank rank_tile(const int32_t *indices, int n_pairs, int E, int key_bits,
+                                     int p, int32_t *wave_cnt, uint32_t *ctrl, bool flag_errors)
+{
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
-    const int E = a.num_experts;
-    const int tile = blockIdx.x;
-    const int p = tile * kRouteTile + tid;
-    int32_t *wave_cnt = lds;                     // [kRouteWaves][E]
-    int32_t *eoff = lds + kRouteWaves * E;       // [E+1] (single tile)
-
     for (int i = tid; i < kRouteWaves * E; i += kRouteThreads)
         wave_cnt[i] = 0;
 
     int e = -1;
-    if (p < a.n_pairs) {
-        const int v = a.indices[p];
+    if (p < n_pairs) {
+        const int v = indices[p];
         if (v >= 0 && v < E)
             e = v;
-        else
-            atomicOr(&a.ctrl[kCtrlError], 1u);
+        else if (flag_errors)
+            atomicOr(&ctrl[kCtrlError], 1u);
     }
     const bool valid = e >= 0;
 
     // match-any over the expert id bits
     uint64_t match = __ballot(valid);
-    for (int bit = 0; bit < a.key_bits; ++bit) {
+    for (int bit = 0; bit < key_bits; ++bit) {
         const bool one = (e >> bit) & 1;
         const uint64_t ones = __ballot(one);
         match &= one ? ones : ~ones;
@@ -193,30 +196,51 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_rank(RouteArgs a)
     __syncthreads();
 
     // per expert: exclusive prefix over the waves (independent LDS loads
-    // first), and the tile total
-    int col_total = 0;
-    for (int x = tid; x < E; x += kRouteThreads) {
+    // first), and the tile total; E <= kRouteThreads: one expert per thread
+    TileRank r;
+    r.col_total = 0;
+    if (tid < E) {
         int c[kRouteWaves];
 #pragma unroll
         for (int w = 0; w < kRouteWaves; ++w)
-            c[w] = wave_cnt[w * E + x];
+            c[w] = wave_cnt[w * E + tid];
         int run = 0;
 #pragma unroll
         for (int w = 0; w < kRouteWaves; ++w) {
-            wave_cnt[w * E + x] = run;
+            wave_cnt[w * E + tid] = run;
             run += c[w];
         }
-        col_total = run;  // E <= kRouteThreads: one x per thread
-        if (!SINGLE_TILE)
-            a.tile_table[(size_t)tile * E + x] = run;
+        r.col_total = run;
     }
     __syncthreads();
-    if (p < a.n_pairs)
-        a.rank_in_tile[p] = valid ? wave_cnt[wave * E + e] + rank_in_wave : -1;
+    r.e = e;
+    r.rank = valid ? wave_cnt[wave * E + e] + rank_in_wave : -1;
+    return r;
+}
 
-    if (SINGLE_TILE) {
+template <bool SINGLE_TILE>
+__global__ __launch_bounds__(kRouteThreads) void k_route_rank(RouteArgs a)
+{
+    extern __shared__ int32_t lds[];
+    __shared__ int32_t s_wave_tot[kRouteWaves + 1];
+
+    const int tid = threadIdx.x;
+    const int E = a.num_experts;
+    const int tile = blockIdx.x;
+    const int p = tile * kRouteTile + tid;
+    int32_t *wave_cnt = lds;                     // [kRouteWaves][E]
+    int32_t *eoff = lds + kRouteWaves * E;       // [E+1] (single tile)
+
+    const TileRank r = rank_tile(a.indices, a.n_pairs, E, a.key_bits, p, wave_cnt, a.ctrl, true);
+    if (p < a.n_pairs)
+        a.rank_in_tile[p] = r.rank;
+    if (!SINGLE_TILE) {
+        if (tid < E)
+            a.tile_table[(size_t)tile * E + tid] = r.col_total;
+    } else {
         // the only tile: its histogram is the whole histogram
-        write_offsets(a, col_total, eoff, s_wave_tot);
+        write_offsets(E, a.num_ranks, r.col_total, eoff, s_wave_tot, a.expert_off, a.rank_off,
+                      a.recv_count, true);
         if (tid < E)
             a.tile_table[tid] = eoff[tid];
     }
@@ -272,7 +296,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scan(RouteArgs a)
         }
         col_total = run;
     }
-    write_offsets(a, col_total, eoff, s_wave_tot);
+    write_offsets(E, a.num_ranks, col_total, eoff, s_wave_tot, a.expert_off, a.rank_off,
+                  a.recv_count, true);
 
     if (tid < G * E) {
         int run = eoff[col] + part[tid];
@@ -314,6 +339,7 @@ struct ScatterArgs {
     int32_t hidden;              // bf16 elements per row (quantizing kernels)
     int32_t segs;                // row segments per token
     int32_t seg_vecs;            // input vectors per segment (a multiple of 64*CH)
+    int32_t work_waves;          // waves per block that take a (token, segment)
     const int32_t *indices;      // [T, K]
     const int32_t *tile_table;   // first slot per (tile, expert)
     const int32_t *rank_in_tile; // [T*K]
@@ -329,9 +355,63 @@ struct ScatterArgs {
     uint8_t *out_scales;         // [N_cap, scale row] or NULL
     int32_t scale_words;         // 4-byte words per carried scale row
     uint32_t *ctrl;              // error flag
+    // routing outputs, written by the scatter itself when it routes inline
+    int32_t key_bits;
+    int32_t num_ranks;
+    int32_t *expert_off;         // [E+1]
+    int32_t *rank_off;           // [R+1]
+    int32_t *recv_count;         // [R]
 };
 
-// Slot of this lane's pair (lanes < K); `record` also stores slot_of / src_pos.
+// ---- inline routing for a single tile (num_tokens * K <= kRouteTile) ----
+//
+// With at most one routing tile there is nothing to scan across blocks, so
+// the scatter launch routes by itself and dispatch is one launch.  Its blocks
+// have kRouteThreads threads: every block ranks the whole tile exactly like
+// k_route_rank (one pair per thread) and scans the histogram into expert
+// offsets, all in LDS, then its first work_waves waves copy their (token,
+// segment) pieces with slot = expert_off[e] + rank (fewer copying waves per
+// block spread the copies over more CUs).  Block 0 publishes expert_off /
+// rank_off / recv_count and raises the error flag.
+
+struct InlineRouteLds {
+    int32_t wave_cnt[kRouteWaves * kMaxExperts];
+    int32_t eoff[kMaxExperts + 1];
+    int32_t slot[kRouteTile];
+    int32_t wave_tot[kRouteWaves + 1];
+};
+
+__device__ inline void inline_route(const ScatterArgs &a, InlineRouteLds &l)
+{
+    const int tid = threadIdx.x;
+    const bool first = blockIdx.x == 0;
+    const TileRank r = rank_tile(a.indices, a.n_pairs, a.num_experts, a.key_bits, tid,
+                                 l.wave_cnt, a.ctrl, first);
+    write_offsets(a.num_experts, a.num_ranks, r.col_total, l.eoff, l.wave_tot, a.expert_off,
+                  a.rank_off, a.recv_count, first);
+    l.slot[tid] = r.e >= 0 ? l.eoff[r.e] + r.rank : -1;
+    __syncthreads();
+}
+
+// Slot of this lane's pair (lanes < K) from the block's slot table.
+__device__ inline int pair_slot_inline(const ScatterArgs &a, const InlineRouteLds &l, int t,
+                                       int lane, bool record)
+{
+    int s = -1;
+    if (lane < a.topk) {
+        const int p = t * a.topk + lane;
+        s = l.slot[p];
+        if (record) {
+            if (s >= 0)
+                a.src_pos[s] = p;
+            a.slot_of[p] = s;
+        }
+    }
+    return s;
+}
+
+// Slot of this lane's pair (lanes < K) from the routing table of the
+// two-launch route; `record` also stores slot_of / src_pos.
 __device__ inline int pair_slot(const ScatterArgs &a, int t, int lane, bool record)
 {
     int s = -1;
@@ -395,31 +475,68 @@ struct ScatterWave {
     int lane, t, base, end, slot;
 };
 
-__device__ inline bool scatter_wave(const ScatterArgs &a, int row_vecs, ScatterWave &w)
+// Shared part: token, segment and range of wave `wv`; false if it has no work.
+__device__ inline bool scatter_wave_range(const ScatterArgs &a, int row_vecs, ScatterWave &w,
+                                          int &seg)
 {
     w.lane = threadIdx.x & (kWave - 1);
-    const int wv = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int wave = threadIdx.x / kWave;
+    if (wave >= a.work_waves)
+        return false;
+    const int wv = blockIdx.x * a.work_waves + wave;
     if (wv >= a.num_tokens * a.segs)
         return false;
     w.t = wv / a.segs;
-    const int sg = wv - w.t * a.segs;
-    w.base = sg * a.seg_vecs;
+    seg = wv - w.t * a.segs;
+    w.base = seg * a.seg_vecs;
     w.end = min(row_vecs, w.base + a.seg_vecs);
-    w.slot = pair_slot(a, w.t, w.lane, sg == 0);
-    if (sg == 0)
+    return true;
+}
+
+// Slots from the routing table of the two-launch route.
+__device__ inline bool scatter_wave_table(const ScatterArgs &a, int row_vecs, ScatterWave &w)
+{
+    int seg;
+    if (!scatter_wave_range(a, row_vecs, w, seg))
+        return false;
+    w.slot = pair_slot(a, w.t, w.lane, seg == 0);
+    if (seg == 0)
         carry_small_rows(a, w.t, w.slot, w.lane);
     return true;
+}
+
+// Slots routed by this block itself (a single tile; kRouteThreads threads).
+__device__ inline bool scatter_wave_inline(const ScatterArgs &a, int row_vecs, ScatterWave &w)
+{
+    __shared__ InlineRouteLds l;
+    inline_route(a, l);  // whole block, before any wave leaves
+    int seg;
+    if (!scatter_wave_range(a, row_vecs, w, seg))
+        return false;
+    w.slot = pair_slot_inline(a, l, w.t, w.lane, seg == 0);
+    if (seg == 0)
+        carry_small_rows(a, w.t, w.slot, w.lane);
+    return true;
+}
+
+template <bool INLINE>
+__device__ inline bool scatter_wave(const ScatterArgs &a, int row_vecs, ScatterWave &w)
+{
+    if constexpr (INLINE)
+        return scatter_wave_inline(a, row_vecs, w);
+    else
+        return scatter_wave_table(a, row_vecs, w);
 }
 
 // bf16 or raw rows: 16-byte nontemporal loads once, K rows of ordinary 16-byte
 // stores (on gfx950 ordinary stores stream this 1->K pattern to HBM faster
 // than nontemporal ones).
-template <int CH>
-__global__ __launch_bounds__(256) void k_scatter_copy(ScatterArgs a)
+template <int CH, bool INLINE = false>
+__global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_copy(ScatterArgs a)
 {
     const int V = a.in_row_vecs;
     ScatterWave w;
-    if (!scatter_wave(a, V, w))
+    if (!scatter_wave<INLINE>(a, V, w))
         return;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)w.t * V;
     u32x4 *out = reinterpret_cast<u32x4 *>(a.out);
@@ -448,13 +565,13 @@ __global__ __launch_bounds__(256) void k_scatter_copy(ScatterArgs a)
 
 // OCP E4M3 with one fp32 scale per 128 elements (16 lanes x 8 elements).
 // Segments are whole numbers of 16-vector blocks.
-template <int CH>
-__global__ __launch_bounds__(256) void k_scatter_fp8(ScatterArgs a)
+template <int CH, bool INLINE = false>
+__global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_fp8(ScatterArgs a)
 {
     const int V = a.hidden / 8;          // 8 bf16 per vector
     const int nblk = a.hidden / 128;     // scales per row
     ScatterWave w;
-    if (!scatter_wave(a, V, w))
+    if (!scatter_wave<INLINE>(a, V, w))
         return;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)w.t * V;
     for (int b = w.base; b < w.end; b += kWave * CH) {
@@ -510,13 +627,13 @@ __global__ __launch_bounds__(256) void k_scatter_fp8(ScatterArgs a)
 
 // MXFP4: E2M1 pairs via v_cvt_scalef32_pk_fp4_f32, one E8M0 scale per 32
 // elements (4 lanes x 8 elements).
-template <int CH>
-__global__ __launch_bounds__(256) void k_scatter_mxfp4(ScatterArgs a)
+template <int CH, bool INLINE = false>
+__global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_mxfp4(ScatterArgs a)
 {
     const int V = a.hidden / 8;
     const int nblk = a.hidden / 32;
     ScatterWave w;
-    if (!scatter_wave(a, V, w))
+    if (!scatter_wave<INLINE>(a, V, w))
         return;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)w.t * V;
     for (int b = w.base; b < w.end; b += kWave * CH) {
@@ -615,7 +732,7 @@ __device__ inline void accumulate_row(float *acc, float w, u32x4 x)
 // KT = K known at compile time (double-buffered), or 0: runtime K <= kMaxTopk.
 // CH 16-byte vectors per lane per segment; segments are 64*CH vectors.
 template <int KT, int CH = kCombineSeg>
-__global__ __launch_bounds__(1024) void k_combine(CombineArgs a)
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;

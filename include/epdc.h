@@ -103,7 +103,10 @@ typedef struct epdc_op epdc_op;
 /* Kernel ids for the profiling calls below. */
 enum {
     EPDC_KERNEL_ROUTE = 0,         /* per-tile histograms + stable in-tile ranks
-                                      (and the scan, when there is one tile) */
+                                      (and the scan, when there is one tile; a
+                                      dispatch of at most 1024 pairs routes inside
+                                      its scatter launch instead, so it records
+                                      only the scatter kernel) */
     EPDC_KERNEL_ROUTE_SCAN = 1,    /* scan to expert/rank offsets + tile bases */
     EPDC_KERNEL_SCATTER = 2,       /* slot + row copy (bf16 or raw) */
     EPDC_KERNEL_SCATTER_FP8 = 3,   /* slot + E4M3 quantize + copy */

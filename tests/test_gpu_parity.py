@@ -157,23 +157,25 @@ def test_zero_tokens():
     assert y.shape == (0, 256) and yw.shape == (0, 4)
 
 
-def test_invalid_expert_ids_get_no_slot():
-    log("invalid ids")
+@pytest.mark.parametrize("T", [300, 200])   # 1200 pairs: two routing tiles; 800: routed inline
+def test_invalid_expert_ids_get_no_slot(T):
+    log(f"invalid ids T={T}")
     rng = np.random.default_rng(21)
-    T, H, K, E, R = 300, 64, 4, 16, 4
+    H, K, E, R = 64, 4, 16, 4
     x = wl.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     idx = rng.integers(0, E, (T, K)).astype(np.int32)
-    idx[5, 2], idx[100, 0], idx[299, 3] = -1, E, 1 << 30
+    idx[5, 2], idx[100, 0], idx[T - 1, 3] = -1, E, 1 << 30
     wts = rng.random((T, K)).astype(np.float32)
     op, ref = run_case(x, wts, idx, E, R)
     assert ref["invalid"] == 3
     assert op.device_error() == 0   # the flag was cleared by the read inside run_case
 
 
-def test_all_pairs_one_expert_and_empty_ranks():
-    log("one expert")
+@pytest.mark.parametrize("T", [700, 300])   # 2100 pairs: three tiles; 900: routed inline
+def test_all_pairs_one_expert_and_empty_ranks(T):
+    log(f"one expert T={T}")
     rng = np.random.default_rng(22)
-    T, H, K, E, R = 700, 128, 3, 32, 8
+    H, K, E, R = 128, 3, 32, 8
     x = wl.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     idx = np.full((T, K), 9, np.int32)                  # duplicates within a token too
     wts = rng.random((T, K)).astype(np.float32)
@@ -207,11 +209,12 @@ def test_unweighted_combine_and_no_weights():
     run_case(x, None, idx, E, R, weights_none=True)
 
 
-def test_raw_rows_and_carried_scales():
+@pytest.mark.parametrize("T", [513, 100])   # 4104 pairs: five tiles; 800: routed inline
+def test_raw_rows_and_carried_scales(T):
     """Already-quantized payloads are carried as bytes with their scales."""
-    log("raw carry")
+    log(f"raw carry T={T}")
     rng = np.random.default_rng(24)
-    T, K, E, R = 513, 8, 256, 8
+    K, E, R = 8, 256, 8
     raw = rng.integers(0, 256, (T, 7168), dtype=np.uint8)
     sc = rng.standard_normal((T, 56)).astype(np.float32)
     idx = wl.draw_topk(rng, T, E, K, "zipf", 1.1)
@@ -353,6 +356,21 @@ def test_combine_needs_dispatch():
     with pytest.raises(B.EpdcError) as ei:
         op.get_dispatch_src_token_pos()
     assert ei.value.status == B.EPDC_ERR_BAD_STATE
+
+
+def test_single_tile_dispatch_is_one_launch():
+    """At most 1024 pairs: routing happens inside the scatter launch."""
+    log("single-tile launch count")
+    w = wl.WORKLOADS["decode_bf16"]
+    inp = inputs_for("decode_bf16")
+    op = EpDispatchCombineOp(EpDispatchCombineConfig(w.tokens, w.hidden, w.topk, w.experts,
+                                                     w.ranks), DEV)
+    op.profile_begin(8)
+    out, out_w, _, out_idx, _ = op.dispatch(bf16_dev(inp["x"]), torch.from_numpy(
+        inp["weights"]).to(DEV), None, torch.from_numpy(inp["indices"]).to(DEV))
+    op.combine(out, out_w, out_idx)
+    prof = op.profile_end()
+    assert set(prof) == {"k_scatter_copy", "k_combine"}
 
 
 def test_profile_events_time_every_kernel():
