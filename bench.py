@@ -115,6 +115,9 @@ def main() -> int:
                          "second pass of the same number of steps right after them: each "
                          "event record costs about 3.5 us of GPU time, which would inflate "
                          "the step time")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and replay it in the timed loop "
+                         "(the per-kernel event pass stays eager)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the steps "
                          "(a known-size kernel for scaling rocprofv3 byte counters)")
@@ -167,26 +170,44 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    timed_step = step
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            g_out = step()
+        torch.cuda.synchronize()
+
+        def timed_step():
+            graph.replay()
+            return g_out
+        for _ in range(args.warmup):
+            timed_step()
+        torch.cuda.synchronize()
     print(f"bench: warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr,
           flush=True)
 
     stream = torch.cuda.current_stream(dev)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    timed_events = args.kernel_events == "timed"
+    timed_events = args.kernel_events == "timed" and not args.graph
     if timed_events:
         op.profile_begin(4 * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        y, y_w = step()
+        y, y_w = timed_step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     if not timed_events:
         op.profile_begin(4 * args.steps)
         for _ in range(args.steps):
-            y, y_w = step()
+            step()
         torch.cuda.synchronize()
     prof = op.profile_end()
     ms_step_events = ev0.elapsed_time(ev1) / args.steps
@@ -231,7 +252,8 @@ def main() -> int:
                    "quant": w.quant,
                    "combine_input": "identity (dispatch output)" if identity
                    else "independent N(0,1) bf16 rows",
-                   "graph_mode": "eager", "gpu": torch.cuda.get_device_name(dev)},
+                   "graph_mode": "hip graph replay" if args.graph else "eager",
+                   "gpu": torch.cuda.get_device_name(dev)},
         "step_alg_bytes": step_bytes,
         "step_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_frac_of_hbm_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,

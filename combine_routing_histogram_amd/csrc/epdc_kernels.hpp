@@ -475,11 +475,12 @@ struct ScatterWave {
     int lane, t, base, end, slot;
 };
 
-// Shared part: token, segment and range of wave `wv`; false if it has no work.
+// Token, segment and range of this wave; false if it has no work.
 __device__ inline bool scatter_wave_range(const ScatterArgs &a, int row_vecs, ScatterWave &w,
                                           int &seg)
 {
     w.lane = threadIdx.x & (kWave - 1);
+    w.slot = -1;
     const int wave = threadIdx.x / kWave;
     if (wave >= a.work_waves)
         return false;
@@ -493,39 +494,31 @@ __device__ inline bool scatter_wave_range(const ScatterArgs &a, int row_vecs, Sc
     return true;
 }
 
-// Slots from the routing table of the two-launch route.
-__device__ inline bool scatter_wave_table(const ScatterArgs &a, int row_vecs, ScatterWave &w)
-{
-    int seg;
-    if (!scatter_wave_range(a, row_vecs, w, seg))
-        return false;
-    w.slot = pair_slot(a, w.t, w.lane, seg == 0);
-    if (seg == 0)
-        carry_small_rows(a, w.t, w.slot, w.lane);
-    return true;
-}
-
-// Slots routed by this block itself (a single tile; kRouteThreads threads).
-__device__ inline bool scatter_wave_inline(const ScatterArgs &a, int row_vecs, ScatterWave &w)
+__device__ inline InlineRouteLds &inline_route_lds()
 {
     __shared__ InlineRouteLds l;
-    inline_route(a, l);  // whole block, before any wave leaves
-    int seg;
-    if (!scatter_wave_range(a, row_vecs, w, seg))
-        return false;
-    w.slot = pair_slot_inline(a, l, w.t, w.lane, seg == 0);
-    if (seg == 0)
-        carry_small_rows(a, w.t, w.slot, w.lane);
-    return true;
+    return l;
 }
 
+// The K slots of the wave's token (lane k holds pair k's slot), recorded by
+// the segment-0 wave, which also carries the small rows.  With INLINE the
+// whole block routes the tile first, waves without work included.  Called
+// after the wave's first loads are in flight, so their latency overlaps the
+// routing.
 template <bool INLINE>
-__device__ inline bool scatter_wave(const ScatterArgs &a, int row_vecs, ScatterWave &w)
+__device__ inline void route_wave(const ScatterArgs &a, bool has_work, int seg, ScatterWave &w)
 {
-    if constexpr (INLINE)
-        return scatter_wave_inline(a, row_vecs, w);
-    else
-        return scatter_wave_table(a, row_vecs, w);
+    if constexpr (INLINE) {
+        InlineRouteLds &l = inline_route_lds();
+        inline_route(a, l);
+        if (has_work)
+            w.slot = pair_slot_inline(a, l, w.t, w.lane, seg == 0);
+    } else {
+        if (has_work)
+            w.slot = pair_slot(a, w.t, w.lane, seg == 0);
+    }
+    if (has_work && seg == 0)
+        carry_small_rows(a, w.t, w.slot, w.lane);
 }
 
 // bf16 or raw rows: 16-byte nontemporal loads once, K rows of ordinary 16-byte
@@ -536,18 +529,27 @@ __global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_copy(S
 {
     const int V = a.in_row_vecs;
     ScatterWave w;
-    if (!scatter_wave<INLINE>(a, V, w))
-        return;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)w.t * V;
+    int seg = 0;
+    const bool has_work = scatter_wave_range(a, V, w, seg);
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)(has_work ? w.t : 0) * V;
     u32x4 *out = reinterpret_cast<u32x4 *>(a.out);
-    for (int b = w.base; b < w.end; b += kWave * CH) {
-        u32x4 v[CH];
+    u32x4 v[CH];
+    auto load = [&](int b) {
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const int j = b + w.lane + kWave * i;
             if (j < w.end)
                 v[i] = __builtin_nontemporal_load(src + j);
         }
+    };
+    if (has_work)
+        load(w.base);
+    route_wave<INLINE>(a, has_work, seg, w);
+    if (!has_work)
+        return;
+    for (int b = w.base; b < w.end; b += kWave * CH) {
+        if (b != w.base)
+            load(b);
         for (int k = 0; k < a.topk; ++k) {
             const int s = read_lane(w.slot, k);
             if (s < 0)
@@ -565,23 +567,15 @@ __global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_copy(S
 
 // OCP E4M3 with one fp32 scale per 128 elements (16 lanes x 8 elements).
 // Segments are whole numbers of 16-vector blocks.
-template <int CH, bool INLINE = false>
-__global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_fp8(ScatterArgs a)
+template <int CH>
+__device__ inline void quant_fp8_pass(const u32x4 *src, int b, int end, int lane, u32x2 *code,
+                                      float *scale)
 {
-    const int V = a.hidden / 8;          // 8 bf16 per vector
-    const int nblk = a.hidden / 128;     // scales per row
-    ScatterWave w;
-    if (!scatter_wave<INLINE>(a, V, w))
-        return;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)w.t * V;
-    for (int b = w.base; b < w.end; b += kWave * CH) {
-    u32x2 code[CH];
-    float scale[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-        const int j = b + w.lane + kWave * i;
+        const int j = b + lane + kWave * i;
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (j < w.end)
+        if (j < end)
             v = __builtin_nontemporal_load(src + j);
         float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                       bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
@@ -589,7 +583,8 @@ __global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_fp8(Sc
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             m = fmaxf(m, fabsf(x[q]));
-        // V is a multiple of 16, so the 16 lanes of a block are all in or all out
+        // the segment end is a multiple of 16 vectors, so the 16 lanes of a
+        // block are all in or all out
         m = fmaxf(m, __shfl_xor(m, 1, kWave));
         m = fmaxf(m, __shfl_xor(m, 2, kWave));
         m = fmaxf(m, __shfl_xor(m, 4, kWave));
@@ -606,44 +601,57 @@ __global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_fp8(Sc
         code[i] = u32x2{lo, hi};
         scale[i] = s;
     }
-    for (int k = 0; k < a.topk; ++k) {
-        const int s = read_lane(w.slot, k);
-        if (s < 0)
-            continue;
-        u32x2 *dst = reinterpret_cast<u32x2 *>(a.out + (size_t)s * a.hidden);
-        float *dsc = reinterpret_cast<float *>(a.out_scales) + (size_t)s * nblk;
+}
+
+template <int CH, bool INLINE = false>
+__global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_fp8(ScatterArgs a)
+{
+    const int V = a.hidden / 8;          // 8 bf16 per vector
+    const int nblk = a.hidden / 128;     // scales per row
+    ScatterWave w;
+    int seg = 0;
+    const bool has_work = scatter_wave_range(a, V, w, seg);
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)(has_work ? w.t : 0) * V;
+    u32x2 code[CH];
+    float scale[CH];
+    if (has_work)
+        quant_fp8_pass<CH>(src, w.base, w.end, w.lane, code, scale);
+    route_wave<INLINE>(a, has_work, seg, w);
+    if (!has_work)
+        return;
+    for (int b = w.base; b < w.end; b += kWave * CH) {
+        if (b != w.base)
+            quant_fp8_pass<CH>(src, b, w.end, w.lane, code, scale);
+        for (int k = 0; k < a.topk; ++k) {
+            const int s = read_lane(w.slot, k);
+            if (s < 0)
+                continue;
+            u32x2 *dst = reinterpret_cast<u32x2 *>(a.out + (size_t)s * a.hidden);
+            float *dsc = reinterpret_cast<float *>(a.out_scales) + (size_t)s * nblk;
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int j = b + w.lane + kWave * i;
-            if (j < w.end) {
-                dst[j] = code[i];
-                if ((w.lane & 15) == 0)
-                    dsc[j >> 4] = scale[i];
+            for (int i = 0; i < CH; ++i) {
+                const int j = b + w.lane + kWave * i;
+                if (j < w.end) {
+                    dst[j] = code[i];
+                    if ((w.lane & 15) == 0)
+                        dsc[j >> 4] = scale[i];
+                }
             }
         }
-    }
     }
 }
 
 // MXFP4: E2M1 pairs via v_cvt_scalef32_pk_fp4_f32, one E8M0 scale per 32
 // elements (4 lanes x 8 elements).
-template <int CH, bool INLINE = false>
-__global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_mxfp4(ScatterArgs a)
+template <int CH>
+__device__ inline void quant_mxfp4_pass(const u32x4 *src, int b, int end, int lane,
+                                        uint32_t *code, uint32_t *sbyte)
 {
-    const int V = a.hidden / 8;
-    const int nblk = a.hidden / 32;
-    ScatterWave w;
-    if (!scatter_wave<INLINE>(a, V, w))
-        return;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)w.t * V;
-    for (int b = w.base; b < w.end; b += kWave * CH) {
-    uint32_t code[CH];
-    uint32_t sbyte[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-        const int j = b + w.lane + kWave * i;
+        const int j = b + lane + kWave * i;
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (j < w.end)
+        if (j < end)
             v = __builtin_nontemporal_load(src + j);
         float x[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                       bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
@@ -666,22 +674,43 @@ __global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_mxfp4(
         code[i] = q;
         sbyte[i] = sb;
     }
-    for (int k = 0; k < a.topk; ++k) {
-        const int s = read_lane(w.slot, k);
-        if (s < 0)
-            continue;
-        uint32_t *dst = reinterpret_cast<uint32_t *>(a.out + (size_t)s * (a.hidden / 2));
-        uint8_t *dsc = a.out_scales + (size_t)s * nblk;
+}
+
+template <int CH, bool INLINE = false>
+__global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_mxfp4(ScatterArgs a)
+{
+    const int V = a.hidden / 8;
+    const int nblk = a.hidden / 32;
+    ScatterWave w;
+    int seg = 0;
+    const bool has_work = scatter_wave_range(a, V, w, seg);
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.input) + (size_t)(has_work ? w.t : 0) * V;
+    uint32_t code[CH];
+    uint32_t sbyte[CH];
+    if (has_work)
+        quant_mxfp4_pass<CH>(src, w.base, w.end, w.lane, code, sbyte);
+    route_wave<INLINE>(a, has_work, seg, w);
+    if (!has_work)
+        return;
+    for (int b = w.base; b < w.end; b += kWave * CH) {
+        if (b != w.base)
+            quant_mxfp4_pass<CH>(src, b, w.end, w.lane, code, sbyte);
+        for (int k = 0; k < a.topk; ++k) {
+            const int s = read_lane(w.slot, k);
+            if (s < 0)
+                continue;
+            uint32_t *dst = reinterpret_cast<uint32_t *>(a.out + (size_t)s * (a.hidden / 2));
+            uint8_t *dsc = a.out_scales + (size_t)s * nblk;
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int j = b + w.lane + kWave * i;
-            if (j < w.end) {
-                dst[j] = code[i];
-                if ((w.lane & 3) == 0)
-                    dsc[j >> 2] = (uint8_t)sbyte[i];
+            for (int i = 0; i < CH; ++i) {
+                const int j = b + w.lane + kWave * i;
+                if (j < w.end) {
+                    dst[j] = code[i];
+                    if ((w.lane & 3) == 0)
+                        dsc[j >> 2] = (uint8_t)sbyte[i];
+                }
             }
         }
-    }
     }
 }
 
