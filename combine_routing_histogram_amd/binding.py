@@ -67,6 +67,11 @@ _SIGNATURES = {
     "epdc_destroy": (I32, [P]),
     "epdc_dispatch": (I32, [P, P, I32, P, P, P, P, P, P, P, P, P]),
     "epdc_combine": (I32, [P, P, P, P, P, P, P]),
+    "epdc_dispatch_replay": (I32, [P, P, P, P, P, P, P, P]),
+    "epdc_dispatch_send": (I32, [P, P, I32, P, P, P, P, P, P, P, P, P]),
+    "epdc_dispatch_recv": (I32, [P, P]),
+    "epdc_combine_send": (I32, [P, P, P, P, P, P, P]),
+    "epdc_combine_recv": (I32, [P, P]),
     "epdc_get_dispatch_src_token_pos": (I32, [P, ctypes.POINTER(P), PI32]),
     "epdc_get_routing": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P)]),
     "epdc_get_device_error": (I32, [P, P, PI32]),
@@ -153,6 +158,36 @@ def epdc_combine(op: int, stream: int, input: int, weights: int, indices: int, o
                  out_weights: int) -> None:
     _check(lib().epdc_combine(op, stream or None, input or None, weights or None,
                               indices or None, output or None, out_weights or None))
+
+
+def epdc_dispatch_replay(op: int, stream: int, input: int, weights: int, scales: int, out: int,
+                         out_weights: int, out_scales: int) -> None:
+    _check(lib().epdc_dispatch_replay(op, stream or None, input or None, weights or None,
+                                      scales or None, out or None, out_weights or None,
+                                      out_scales or None))
+
+
+def epdc_dispatch_send(op: int, stream: int, num_tokens: int, input: int, weights: int,
+                       scales: int, indices: int, out: int, out_weights: int, out_scales: int,
+                       out_indices: int, recv_count: int) -> None:
+    _check(lib().epdc_dispatch_send(op, stream or None, num_tokens, input or None,
+                                    weights or None, scales or None, indices or None,
+                                    out or None, out_weights or None, out_scales or None,
+                                    out_indices or None, recv_count or None))
+
+
+def epdc_dispatch_recv(op: int, stream: int) -> None:
+    _check(lib().epdc_dispatch_recv(op, stream or None))
+
+
+def epdc_combine_send(op: int, stream: int, input: int, weights: int, indices: int, output: int,
+                      out_weights: int) -> None:
+    _check(lib().epdc_combine_send(op, stream or None, input or None, weights or None,
+                                   indices or None, output or None, out_weights or None))
+
+
+def epdc_combine_recv(op: int, stream: int) -> None:
+    _check(lib().epdc_combine_recv(op, stream or None))
 
 
 def epdc_get_dispatch_src_token_pos(op: int) -> Tuple[int, int]:

@@ -151,6 +151,9 @@ struct epdc_op {
     int key_bits;
     bool routed;
     int32_t last_tokens;
+    // split-phase completion markers (timing disabled)
+    hipEvent_t ev_dispatch, ev_combine;
+    bool dispatch_sent, combine_sent;
     // per-kernel timing
     bool profiling;
     int ev_cap, ev_used;
@@ -239,6 +242,67 @@ epdc_status grid_for_waves(int64_t waves, int *grid, int *block)
     return EPDC_SUCCESS;
 }
 
+// Plan, grid and launch of the scatter kernel for the op's payload kind;
+// sa holds everything but the plan fields.
+epdc_status launch_scatter(epdc_op *op, hipStream_t st, ScatterArgs &sa, int mode)
+{
+    const epdc_config &c = op->cfg;
+    const int num_tokens = sa.num_tokens;
+    const bool inline_route = mode == kRouteInline;
+    const int in_vecs = c.quant == EPDC_QUANT_NONE ? sa.in_row_vecs : c.hidden / 8;
+    const ScatterPlan plan = plan_scatter(c.quant, num_tokens, in_vecs, inline_route);
+    sa.segs = plan.segs;
+    sa.seg_vecs = plan.seg_vecs;
+    int grid, block;
+    const int64_t waves = (int64_t)num_tokens * sa.segs;
+    if (inline_route) {
+        // kRouteThreads threads per block for the ranking; about 256 blocks
+        // share the copies (waves <= 1024 * 64 here: at most one tile of pairs)
+        sa.work_waves =
+            (int)std::min<int64_t>(kRouteWaves, std::max<int64_t>(1, (waves + 255) / 256));
+        grid = (int)((waves + sa.work_waves - 1) / sa.work_waves);
+        block = kRouteThreads;
+    } else {
+        epdc_status s = grid_for_waves(waves, &grid, &block);
+        if (s != EPDC_SUCCESS)
+            return s;
+        sa.work_waves = block / kWave;
+    }
+    switch (c.quant) {
+    case EPDC_QUANT_FP8_E4M3_B128:
+        return launch(op, st, EPDC_KERNEL_SCATTER_FP8, [&] {
+            if (mode == kRouteInline)
+                k_scatter_fp8<1, kRouteInline><<<grid, block, 0, st>>>(sa);
+            else if (mode == kRouteReplay)
+                k_scatter_fp8<1, kRouteReplay><<<grid, block, 0, st>>>(sa);
+            else
+                k_scatter_fp8<1><<<grid, block, 0, st>>>(sa);
+        });
+    case EPDC_QUANT_MXFP4_B32:
+        return launch(op, st, EPDC_KERNEL_SCATTER_MXFP4, [&] {
+            if (mode == kRouteInline)
+                k_scatter_mxfp4<2, kRouteInline><<<grid, block, 0, st>>>(sa);
+            else if (mode == kRouteReplay)
+                k_scatter_mxfp4<2, kRouteReplay><<<grid, block, 0, st>>>(sa);
+            else
+                k_scatter_mxfp4<2><<<grid, block, 0, st>>>(sa);
+        });
+    default:
+        return launch(op, st, EPDC_KERNEL_SCATTER, [&] {
+            if (mode == kRouteInline)
+                k_scatter_copy<2, kRouteInline><<<grid, block, 0, st>>>(sa);
+            else if (plan.ch == 8 && mode == kRouteReplay)
+                k_scatter_copy<8, kRouteReplay><<<grid, block, 0, st>>>(sa);
+            else if (mode == kRouteReplay)
+                k_scatter_copy<2, kRouteReplay><<<grid, block, 0, st>>>(sa);
+            else if (plan.ch == 8)
+                k_scatter_copy<8><<<grid, block, 0, st>>>(sa);
+            else
+                k_scatter_copy<2><<<grid, block, 0, st>>>(sa);
+        });
+    }
+}
+
 template <int KT>
 void launch_combine(int grid, int block, hipStream_t st, const CombineArgs &a)
 {
@@ -303,8 +367,21 @@ epdc_status epdc_create(const epdc_config *cfg, void *workspace, size_t workspac
     if (e != hipSuccess)
         return fail(EPDC_ERR_GPU_OP, "clearing control words: %s", hipGetErrorString(e));
 
+    hipEvent_t ev_d = nullptr, ev_c = nullptr;
+    e = hipEventCreateWithFlags(&ev_d, hipEventDisableTiming);
+    if (e == hipSuccess)
+        e = hipEventCreateWithFlags(&ev_c, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        if (ev_d)
+            (void)hipEventDestroy(ev_d);
+        return fail(EPDC_ERR_GPU_OP, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
+    }
+
     epdc_op *o = new epdc_op();
     o->cfg = *cfg;
+    o->ev_dispatch = ev_d;
+    o->ev_combine = ev_c;
+    o->dispatch_sent = o->combine_sent = false;
     o->device = dev;
     o->ws = static_cast<uint8_t *>(workspace);
     o->lay = lay;
@@ -326,6 +403,8 @@ epdc_status epdc_destroy(epdc_op *op)
         return ok();
     for (hipEvent_t ev : op->ev)
         (void)hipEventDestroy(ev);
+    (void)hipEventDestroy(op->ev_dispatch);
+    (void)hipEventDestroy(op->ev_combine);
     delete op;
     return ok();
 }
@@ -408,10 +487,11 @@ epdc_status epdc_dispatch(epdc_op *op, void *stream, int32_t num_tokens, const v
     if (s != EPDC_SUCCESS)
         return s;
 
-    op->routed = true;
-    op->last_tokens = num_tokens;
-    if (num_tokens == 0)
+    if (num_tokens == 0) {
+        op->routed = true;
+        op->last_tokens = 0;
         return ok();
+    }
 
     ScatterArgs sa;
     sa.num_tokens = num_tokens;
@@ -440,54 +520,11 @@ epdc_status epdc_dispatch(epdc_op *op, void *stream, int32_t num_tokens, const v
     sa.rank_off = ra.rank_off;
     sa.recv_count = recv_count;
 
-    const int in_vecs = c.quant == EPDC_QUANT_NONE ? sa.in_row_vecs : c.hidden / 8;
-    const ScatterPlan plan = plan_scatter(c.quant, num_tokens, in_vecs, inline_route);
-    sa.segs = plan.segs;
-    sa.seg_vecs = plan.seg_vecs;
-    int grid, block;
-    const int64_t waves = (int64_t)num_tokens * sa.segs;
-    if (inline_route) {
-        // kRouteThreads threads per block for the ranking; about 256 blocks
-        // share the copies (waves <= 1024 * 64 here: at most one tile of pairs)
-        sa.work_waves = (int)std::min<int64_t>(kRouteWaves, std::max<int64_t>(1, (waves + 255) / 256));
-        grid = (int)((waves + sa.work_waves - 1) / sa.work_waves);
-        block = kRouteThreads;
-    } else {
-        s = grid_for_waves(waves, &grid, &block);
-        if (s != EPDC_SUCCESS)
-            return s;
-        sa.work_waves = block / kWave;
-    }
-    switch (c.quant) {
-    case EPDC_QUANT_FP8_E4M3_B128:
-        s = launch(op, st, EPDC_KERNEL_SCATTER_FP8, [&] {
-            if (inline_route)
-                k_scatter_fp8<1, true><<<grid, block, 0, st>>>(sa);
-            else
-                k_scatter_fp8<1><<<grid, block, 0, st>>>(sa);
-        });
-        break;
-    case EPDC_QUANT_MXFP4_B32:
-        s = launch(op, st, EPDC_KERNEL_SCATTER_MXFP4, [&] {
-            if (inline_route)
-                k_scatter_mxfp4<2, true><<<grid, block, 0, st>>>(sa);
-            else
-                k_scatter_mxfp4<2><<<grid, block, 0, st>>>(sa);
-        });
-        break;
-    default:
-        s = launch(op, st, EPDC_KERNEL_SCATTER, [&] {
-            if (inline_route)
-                k_scatter_copy<2, true><<<grid, block, 0, st>>>(sa);
-            else if (plan.ch == 8)
-                k_scatter_copy<8><<<grid, block, 0, st>>>(sa);
-            else
-                k_scatter_copy<2><<<grid, block, 0, st>>>(sa);
-        });
-        break;
-    }
+    s = launch_scatter(op, st, sa, inline_route ? kRouteInline : kRouteTable);
     if (s != EPDC_SUCCESS)
         return s;
+    op->routed = true;
+    op->last_tokens = num_tokens;
     return ok();
 }
 
@@ -538,6 +575,109 @@ epdc_status epdc_combine(epdc_op *op, void *stream, const void *input, const flo
     });
     if (s != EPDC_SUCCESS)
         return s;
+    return ok();
+}
+
+epdc_status epdc_dispatch_replay(epdc_op *op, void *stream, const void *input,
+                                 const float *weights, const void *scales, void *out,
+                                 float *out_weights, void *out_scales)
+{
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    if (!op->routed)
+        return fail(EPDC_ERR_BAD_STATE, "routing replay needs a dispatch first");
+    const epdc_config &c = op->cfg;
+    const int T = op->last_tokens;
+    if (T == 0)
+        return ok();
+    if (!input || !out)
+        return fail(EPDC_ERR_INVALID_ARGS, "input and out are required");
+    if ((weights == nullptr) != (out_weights == nullptr))
+        return fail(EPDC_ERR_INVALID_ARGS, "weights and out_weights must both be given or both NULL");
+    const bool quant = c.quant != EPDC_QUANT_NONE;
+    if (quant && (scales || !out_scales))
+        return fail(EPDC_ERR_INVALID_ARGS,
+                    "quantizing replay produces the scales: scales NULL, out_scales required");
+    if (!quant && scales && (c.scale_row_bytes == 0 || !out_scales))
+        return fail(EPDC_ERR_INVALID_ARGS, "carried scales need scale_row_bytes and out_scales");
+    if (!aligned(input, 16) || !aligned(out, 16) || !aligned(weights, 4) || !aligned(scales, 4) ||
+        !aligned(out_weights, 4) || !aligned(out_scales, 4))
+        return fail(EPDC_ERR_INVALID_ARGS,
+                    "input/out must be 16-byte aligned, the other arrays 4-byte aligned");
+
+    ScatterArgs sa = {};
+    sa.num_tokens = T;
+    sa.n_pairs = T * c.topk;
+    sa.topk = c.topk;
+    sa.num_experts = c.num_experts;
+    sa.hidden = c.hidden;
+    sa.slot_of = op->i32(op->lay.slot_of);
+    sa.input = static_cast<const uint8_t *>(input);
+    sa.in_row_vecs = c.input_kind == EPDC_IN_RAW ? c.raw_row_bytes / 16 : c.hidden / 8;
+    sa.out = static_cast<uint8_t *>(out);
+    sa.weights = weights;
+    sa.out_weights = out_weights;
+    sa.out_indices = nullptr;  // the recorded dispatch already carried the indices
+    sa.scales = quant ? nullptr : static_cast<const uint8_t *>(scales);
+    sa.out_scales = static_cast<uint8_t *>(out_scales);
+    sa.scale_words = c.scale_row_bytes / 4;
+    sa.ctrl = op->ctrl();
+    epdc_status s = launch_scatter(op, static_cast<hipStream_t>(stream), sa, kRouteReplay);
+    return s == EPDC_SUCCESS ? ok() : s;
+}
+
+epdc_status epdc_dispatch_send(epdc_op *op, void *stream, int32_t num_tokens, const void *input,
+                               const float *weights, const void *scales, const int32_t *indices,
+                               void *out, float *out_weights, void *out_scales,
+                               int32_t *out_indices, int32_t *recv_count)
+{
+    epdc_status s = epdc_dispatch(op, stream, num_tokens, input, weights, scales, indices, out,
+                                  out_weights, out_scales, out_indices, recv_count);
+    if (s != EPDC_SUCCESS)
+        return s;
+    const hipError_t e = hipEventRecord(op->ev_dispatch, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(EPDC_ERR_GPU_OP, "hipEventRecord: %s", hipGetErrorString(e));
+    op->dispatch_sent = true;
+    return ok();
+}
+
+epdc_status epdc_dispatch_recv(epdc_op *op, void *stream)
+{
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    if (!op->dispatch_sent)
+        return fail(EPDC_ERR_BAD_STATE, "dispatch_recv without a dispatch_send");
+    const hipError_t e = hipStreamWaitEvent(static_cast<hipStream_t>(stream), op->ev_dispatch, 0);
+    if (e != hipSuccess)
+        return fail(EPDC_ERR_GPU_OP, "hipStreamWaitEvent: %s", hipGetErrorString(e));
+    op->dispatch_sent = false;
+    return ok();
+}
+
+epdc_status epdc_combine_send(epdc_op *op, void *stream, const void *input, const float *weights,
+                              const int32_t *indices, void *output, float *out_weights)
+{
+    epdc_status s = epdc_combine(op, stream, input, weights, indices, output, out_weights);
+    if (s != EPDC_SUCCESS)
+        return s;
+    const hipError_t e = hipEventRecord(op->ev_combine, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(EPDC_ERR_GPU_OP, "hipEventRecord: %s", hipGetErrorString(e));
+    op->combine_sent = true;
+    return ok();
+}
+
+epdc_status epdc_combine_recv(epdc_op *op, void *stream)
+{
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    if (!op->combine_sent)
+        return fail(EPDC_ERR_BAD_STATE, "combine_recv without a combine_send");
+    const hipError_t e = hipStreamWaitEvent(static_cast<hipStream_t>(stream), op->ev_combine, 0);
+    if (e != hipSuccess)
+        return fail(EPDC_ERR_GPU_OP, "hipStreamWaitEvent: %s", hipGetErrorString(e));
+    op->combine_sent = false;
     return ok();
 }
 
@@ -593,6 +733,7 @@ epdc_status epdc_reset(epdc_op *op)
         return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
     op->routed = false;
     op->last_tokens = 0;
+    op->dispatch_sent = op->combine_sent = false;
     return ok();
 }
 

@@ -500,19 +500,37 @@ __device__ inline InlineRouteLds &inline_route_lds()
     return l;
 }
 
+// Where a scatter launch takes its slots from.
+enum {
+    kRouteTable = 0,   // the tile table of the two-launch route
+    kRouteInline = 1,  // routes the single tile itself (kRouteThreads-thread blocks)
+    kRouteReplay = 2   // slot_of of a dispatch recorded earlier (routing replay)
+};
+
 // The K slots of the wave's token (lane k holds pair k's slot), recorded by
-// the segment-0 wave, which also carries the small rows.  With INLINE the
-// whole block routes the tile first, waves without work included.  Called
-// after the wave's first loads are in flight, so their latency overlaps the
-// routing.
-template <bool INLINE>
+// the segment-0 wave, which also carries the small rows.  With kRouteInline
+// the whole block routes the tile first, waves without work included.
+// Called after the wave's first loads are in flight, so their latency
+// overlaps the routing.
+template <int MODE>
 __device__ inline void route_wave(const ScatterArgs &a, bool has_work, int seg, ScatterWave &w)
 {
-    if constexpr (INLINE) {
+    if constexpr (MODE == kRouteInline) {
         InlineRouteLds &l = inline_route_lds();
         inline_route(a, l);
         if (has_work)
             w.slot = pair_slot_inline(a, l, w.t, w.lane, seg == 0);
+    } else if constexpr (MODE == kRouteReplay) {
+        if (has_work && w.lane < a.topk) {
+            const int s = a.slot_of[w.t * a.topk + w.lane];
+            // a recorded slot is -1 or in range; a workspace edited since is not trusted
+            if (s >= a.n_pairs || s < -1) {
+                if (seg == 0)
+                    atomicOr(&a.ctrl[kCtrlError], 2u);
+            } else {
+                w.slot = s;
+            }
+        }
     } else {
         if (has_work)
             w.slot = pair_slot(a, w.t, w.lane, seg == 0);
@@ -524,8 +542,8 @@ __device__ inline void route_wave(const ScatterArgs &a, bool has_work, int seg, 
 // bf16 or raw rows: 16-byte nontemporal loads once, K rows of ordinary 16-byte
 // stores (on gfx950 ordinary stores stream this 1->K pattern to HBM faster
 // than nontemporal ones).
-template <int CH, bool INLINE = false>
-__global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_copy(ScatterArgs a)
+template <int CH, int MODE = kRouteTable>
+__global__ __launch_bounds__(MODE == kRouteInline ? kRouteThreads : 256) void k_scatter_copy(ScatterArgs a)
 {
     const int V = a.in_row_vecs;
     ScatterWave w;
@@ -544,7 +562,7 @@ __global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_copy(S
     };
     if (has_work)
         load(w.base);
-    route_wave<INLINE>(a, has_work, seg, w);
+    route_wave<MODE>(a, has_work, seg, w);
     if (!has_work)
         return;
     for (int b = w.base; b < w.end; b += kWave * CH) {
@@ -603,8 +621,8 @@ __device__ inline void quant_fp8_pass(const u32x4 *src, int b, int end, int lane
     }
 }
 
-template <int CH, bool INLINE = false>
-__global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_fp8(ScatterArgs a)
+template <int CH, int MODE = kRouteTable>
+__global__ __launch_bounds__(MODE == kRouteInline ? kRouteThreads : 256) void k_scatter_fp8(ScatterArgs a)
 {
     const int V = a.hidden / 8;          // 8 bf16 per vector
     const int nblk = a.hidden / 128;     // scales per row
@@ -616,7 +634,7 @@ __global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_fp8(Sc
     float scale[CH];
     if (has_work)
         quant_fp8_pass<CH>(src, w.base, w.end, w.lane, code, scale);
-    route_wave<INLINE>(a, has_work, seg, w);
+    route_wave<MODE>(a, has_work, seg, w);
     if (!has_work)
         return;
     for (int b = w.base; b < w.end; b += kWave * CH) {
@@ -676,8 +694,8 @@ __device__ inline void quant_mxfp4_pass(const u32x4 *src, int b, int end, int la
     }
 }
 
-template <int CH, bool INLINE = false>
-__global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_mxfp4(ScatterArgs a)
+template <int CH, int MODE = kRouteTable>
+__global__ __launch_bounds__(MODE == kRouteInline ? kRouteThreads : 256) void k_scatter_mxfp4(ScatterArgs a)
 {
     const int V = a.hidden / 8;
     const int nblk = a.hidden / 32;
@@ -689,7 +707,7 @@ __global__ __launch_bounds__(INLINE ? kRouteThreads : 256) void k_scatter_mxfp4(
     uint32_t sbyte[CH];
     if (has_work)
         quant_mxfp4_pass<CH>(src, w.base, w.end, w.lane, code, sbyte);
-    route_wave<INLINE>(a, has_work, seg, w);
+    route_wave<MODE>(a, has_work, seg, w);
     if (!has_work)
         return;
     for (int b = w.base; b < w.end; b += kWave * CH) {

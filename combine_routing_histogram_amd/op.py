@@ -72,6 +72,9 @@ class EpDispatchCombineOp:
             self._op = B.epdc_create(c, self.workspace.data_ptr(), ws_bytes)
         self._tokens = 0
         self._scales_dtype = None
+        self._side_stream = None
+        self._sent_dispatch = None
+        self._sent_combine = None
 
     def __del__(self):
         op = getattr(self, "_op", None)
@@ -100,20 +103,14 @@ class EpDispatchCombineOp:
         off = ptr - self.workspace.data_ptr()
         return self.workspace[off:off + 4 * count].view(torch.int32)
 
-    # ---- methods table ---------------------------------------------------------------
-    def dispatch(self, input: torch.Tensor, weights: Optional[torch.Tensor],
-                 scales: Optional[torch.Tensor], indices: torch.Tensor):
-        """Route tokens to expert slots.
+    def _side(self) -> torch.cuda.Stream:
+        # default priority: the send phases run here while the caller's stream computes
+        if self._side_stream is None:
+            self._side_stream = torch.cuda.Stream(device=self.device)
+        return self._side_stream
 
-        Returns (output, weights, scales, indices, recv_count) as views of the
-        op's capacity-sized receive buffers (scales is None when there are
-        none).  output is bf16 [N_cap, H] for bf16 input, float8_e4m3fn
-        [N_cap, H] for FP8, uint8 [N_cap, H/2] (packed E2M1) for MXFP4, or
-        uint8 [N_cap, raw_row_bytes] for raw rows.
-        """
+    def _check_payload(self, input, weights, scales, T: int) -> None:
         cfg = self.config
-        T = int(indices.shape[0])
-        self._need(indices, "indices", torch.int32, (T, cfg.topk))
         if cfg.raw_row_bytes:
             self._need(input, "input")
             if input.numel() * input.element_size() != T * cfg.raw_row_bytes:
@@ -127,16 +124,83 @@ class EpDispatchCombineOp:
             if scales.numel() * scales.element_size() != T * cfg.scale_row_bytes:
                 raise ValueError("scales must hold scale_row_bytes per token")
             self._scales_dtype = scales.dtype
-        B.epdc_dispatch(self._op, self._stream(), T, _ptr(input), _ptr(weights), _ptr(scales),
-                        _ptr(indices), _ptr(self._out),
-                        _ptr(self._out_weights) if weights is not None else 0,
-                        _ptr(self._out_scales) if (scales is not None or cfg.quant != "none") else 0,
-                        _ptr(self._out_indices), _ptr(self._recv_count))
-        self._tokens = T
+
+    def _dispatch_ptrs(self, input, weights, scales):
+        quant = self.config.quant != "none"
+        return (_ptr(input), _ptr(weights), _ptr(scales), _ptr(self._out),
+                _ptr(self._out_weights) if weights is not None else 0,
+                _ptr(self._out_scales) if (scales is not None or quant) else 0)
+
+    def _dispatch_views(self, weights, scales):
         return (self.received_payload(),
                 self._out_weights if weights is not None else None,
                 self.received_scales(scales is not None),
                 self._out_indices, self._recv_count)
+
+    # ---- methods table ---------------------------------------------------------------
+    def dispatch(self, input: torch.Tensor, weights: Optional[torch.Tensor],
+                 scales: Optional[torch.Tensor], indices: torch.Tensor):
+        """Route tokens to expert slots.
+
+        Returns (output, weights, scales, indices, recv_count) as views of the
+        op's capacity-sized receive buffers (scales is None when there are
+        none).  output is bf16 [N_cap, H] for bf16 input, float8_e4m3fn
+        [N_cap, H] for FP8, uint8 [N_cap, H/2] (packed E2M1) for MXFP4, or
+        uint8 [N_cap, raw_row_bytes] for raw rows.
+        """
+        T = int(indices.shape[0])
+        self._need(indices, "indices", torch.int32, (T, self.config.topk))
+        self._check_payload(input, weights, scales, T)
+        i, w, s, o, ow, os_ = self._dispatch_ptrs(input, weights, scales)
+        B.epdc_dispatch(self._op, self._stream(), T, i, w, s, _ptr(indices), o, ow, os_,
+                        _ptr(self._out_indices), _ptr(self._recv_count))
+        self._tokens = T
+        return self._dispatch_views(weights, scales)
+
+    def dispatch_replay(self, input: torch.Tensor, weights: Optional[torch.Tensor] = None,
+                        scales: Optional[torch.Tensor] = None):
+        """Dispatch a new payload for the same tokens with the routing of the
+        last dispatch (no histogram, scan or ranking).  Returns the views of
+        dispatch(); indices and recv_count keep the recorded dispatch's values."""
+        T = self._tokens
+        if T == 0:
+            # nothing to move; the library still refuses a replay with no dispatch recorded
+            B.epdc_dispatch_replay(self._op, self._stream(), 0, 0, 0, 0, 0, 0)
+            return self._dispatch_views(weights, scales)
+        self._check_payload(input, weights, scales, T)
+        i, w, s, o, ow, os_ = self._dispatch_ptrs(input, weights, scales)
+        B.epdc_dispatch_replay(self._op, self._stream(), i, w, s, o, ow, os_)
+        return self._dispatch_views(weights, scales)
+
+    def dispatch_send(self, input: torch.Tensor, weights: Optional[torch.Tensor],
+                      scales: Optional[torch.Tensor], indices: torch.Tensor) -> None:
+        """First phase of a split dispatch: enqueue the whole dispatch on the
+        op's side stream (after the work already on the caller's stream) and
+        return at once, so the caller's stream can compute meanwhile."""
+        T = int(indices.shape[0])
+        self._need(indices, "indices", torch.int32, (T, self.config.topk))
+        self._check_payload(input, weights, scales, T)
+        side = self._side()
+        side.wait_stream(torch.cuda.current_stream(self.device))
+        for t in (input, weights, scales, indices):
+            if t is not None:
+                t.record_stream(side)
+        i, w, s, o, ow, os_ = self._dispatch_ptrs(input, weights, scales)
+        B.epdc_dispatch_send(self._op, side.cuda_stream, T, i, w, s, _ptr(indices), o, ow, os_,
+                             _ptr(self._out_indices), _ptr(self._recv_count))
+        self._tokens = T
+        self._sent_dispatch = (weights is not None, scales is not None)
+
+    def dispatch_recv(self):
+        """Second phase: the caller's stream waits for the sent dispatch;
+        returns what dispatch() returns."""
+        if self._sent_dispatch is None:
+            raise B.EpdcError(B.EPDC_ERR_BAD_STATE, "dispatch_recv without a dispatch_send")
+        B.epdc_dispatch_recv(self._op, self._stream())
+        has_w, has_s = self._sent_dispatch
+        self._sent_dispatch = None
+        return (self.received_payload(), self._out_weights if has_w else None,
+                self.received_scales(has_s), self._out_indices, self._recv_count)
 
     def received_payload(self) -> torch.Tensor:
         cfg = self.config
@@ -167,6 +231,36 @@ class EpDispatchCombineOp:
         dispatch (e.g. the dispatch output itself); weights: fp32 [n, K] in
         the received layout or None.  Returns (output bf16 [T, H], weights fp32 [T, K]).
         """
+        self._check_combine(input, weights)
+        B.epdc_combine(self._op, self._stream(), _ptr(input), _ptr(weights), _ptr(indices),
+                       _ptr(self._combined), _ptr(self._combined_weights))
+        T = self._tokens
+        return self._combined[:T], self._combined_weights[:T]
+
+    def combine_send(self, input: torch.Tensor, weights: Optional[torch.Tensor] = None,
+                     indices: Optional[torch.Tensor] = None) -> None:
+        """First phase of a split combine, on the op's side stream (see dispatch_send)."""
+        self._check_combine(input, weights)
+        side = self._side()
+        side.wait_stream(torch.cuda.current_stream(self.device))
+        for t in (input, weights, indices):
+            if t is not None:
+                t.record_stream(side)
+        B.epdc_combine_send(self._op, side.cuda_stream, _ptr(input), _ptr(weights), _ptr(indices),
+                            _ptr(self._combined), _ptr(self._combined_weights))
+        self._sent_combine = True
+
+    def combine_recv(self) -> Tuple[torch.Tensor, torch.Tensor]:
+        """Second phase: the caller's stream waits for the sent combine;
+        returns what combine() returns."""
+        if not self._sent_combine:
+            raise B.EpdcError(B.EPDC_ERR_BAD_STATE, "combine_recv without a combine_send")
+        B.epdc_combine_recv(self._op, self._stream())
+        self._sent_combine = None
+        T = self._tokens
+        return self._combined[:T], self._combined_weights[:T]
+
+    def _check_combine(self, input, weights) -> None:
         cfg = self.config
         self._need(input, "input", torch.bfloat16)
         if input.dim() != 2 or input.shape[1] != cfg.hidden:
@@ -178,14 +272,11 @@ class EpDispatchCombineOp:
             self._need(weights, "weights", torch.float32)
             if weights.dim() != 2 or weights.shape[0] < rows or weights.shape[1] != cfg.topk:
                 raise ValueError(f"combine weights must be [>= {rows}, topk] fp32")
-        B.epdc_combine(self._op, self._stream(), _ptr(input), _ptr(weights), _ptr(indices),
-                       _ptr(self._combined), _ptr(self._combined_weights))
-        T = self._tokens
-        return self._combined[:T], self._combined_weights[:T]
 
     def reset(self) -> None:
         B.epdc_reset(self._op)
         self._tokens = 0
+        self._sent_dispatch = self._sent_combine = None
 
     def get_dispatch_src_token_pos(self) -> torch.Tensor:
         """Per received row, the pair index t*K + k it came from (the first

@@ -183,6 +183,42 @@ epdc_status epdc_combine(epdc_op *op, void *stream, const void *input,
                          const float *weights, const int32_t *indices,
                          void *output, float *out_weights);
 
+/*
+ * Routing replay: dispatch a new payload with the routing recorded by the last
+ * dispatch (same tokens, same expert ids), skipping the histogram, scan and
+ * ranking ("Choosing an EP API and backend" page, "EP paths" table: routing
+ * replay).  Writes the payload, carried weights and scales rows to the same
+ * slots; out_indices, recv_count, the offsets and src_token_pos are those of
+ * the recorded dispatch and are not rewritten.  Arguments as in
+ * epdc_dispatch, for num_tokens = the recorded dispatch's.  BAD_STATE if no
+ * dispatch is recorded.
+ */
+epdc_status epdc_dispatch_replay(epdc_op *op, void *stream, const void *input,
+                                 const float *weights, const void *scales, void *out,
+                                 float *out_weights, void *out_scales);
+
+/*
+ * Split phases for overlapping other work with dispatch and combine
+ * ("Communication APIs" page, methods table: dispatch_send / dispatch_recv,
+ * combine_send / combine_recv; "AsyncLL v2 SDMA overlap" section: data and
+ * counts are ready once the receive phase completes on the stream).  On one
+ * GPU the send phase is the whole operation enqueued on `stream` (typically a
+ * side stream) followed by a completion marker owned by the op; the receive
+ * phase makes `stream` (typically the compute stream) wait for that marker,
+ * without a host wait.  *_send takes the arguments of epdc_dispatch /
+ * epdc_combine; *_recv returns BAD_STATE without a matching send.
+ */
+epdc_status epdc_dispatch_send(epdc_op *op, void *stream, int32_t num_tokens,
+                               const void *input, const float *weights,
+                               const void *scales, const int32_t *indices,
+                               void *out, float *out_weights, void *out_scales,
+                               int32_t *out_indices, int32_t *recv_count);
+epdc_status epdc_dispatch_recv(epdc_op *op, void *stream);
+epdc_status epdc_combine_send(epdc_op *op, void *stream, const void *input,
+                              const float *weights, const int32_t *indices,
+                              void *output, float *out_weights);
+epdc_status epdc_combine_recv(epdc_op *op, void *stream);
+
 /* Device pointer to src_token_pos [T_max*K] int32 of the last dispatch: for
  * slot s < n_valid, the pair index p = t*K + k it came from ("Get source
  * positions of dispatched tokens (for verification)", methods table).
@@ -201,8 +237,9 @@ epdc_status epdc_get_routing(epdc_op *op, const int32_t **expert_off,
  * outside [0, E).  Synchronizes; not for use under graph capture. */
 epdc_status epdc_get_device_error(epdc_op *op, void *stream, int32_t *flag);
 
-/* Forget the recorded routing ("Reset internal state between iterations").
- * No device work: counts need no clearing because dispatch writes them. */
+/* Forget the recorded routing and any unreceived send ("Reset internal state
+ * between iterations").  No device work: counts need no clearing because
+ * dispatch writes them. */
 epdc_status epdc_reset(epdc_op *op);
 
 /* Thread-local message for the last non-SUCCESS status ("" if none). */
