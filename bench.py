@@ -11,6 +11,9 @@ Inputs are resident in HBM before the timed region.  Prints one JSON line.
 value = tokens/s of whole steps.  roofline: the kernel with the most time,
 algorithmic bytes per launch / its mean duration from HIP events recorded on
 the launch stream around each kernel during the timed steps.
+cold_cache: per-kernel event times of a further pass in which writing a
+512 MiB scratch buffer before every step evicts L2 and the MALL (the timed loop reuses its buffers,
+so part of each kernel's data is still cached from the step before).
 cpu_baseline: the CPU oracle (plain C, single thread) on the same workload;
 its last step is also compared bit for bit with the GPU's last timed step.
 """
@@ -121,6 +124,9 @@ def main() -> int:
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the steps "
                          "(a known-size kernel for scaling rocprofv3 byte counters)")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="steps of an extra per-kernel event pass in which writing a 512 MiB "
+                         "scratch buffer before each step evicts L2 and the MALL (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU-oracle baseline (0 = skip)")
     args = ap.parse_args()
@@ -211,6 +217,22 @@ def main() -> int:
         torch.cuda.synchronize()
     prof = op.profile_end()
     ms_step_events = ev0.elapsed_time(ev1) / args.steps
+
+    # Cold-cache pass: the timed loop reuses the same buffers every step, so
+    # part of each kernel's input or output is still in the 256 MB MALL from
+    # the step before.  Here writing a 512 MiB scratch buffer (outside the
+    # kernel events) before every step leaves L2 and the MALL full of other,
+    # dirty lines, as a layer with other work in between would find them.
+    cold = None
+    if args.cold_steps > 0:
+        scratch = torch.empty(256 << 20, dtype=torch.int16, device=dev)
+        op.profile_begin(4 * args.cold_steps)
+        for i in range(args.cold_steps):
+            scratch.fill_(i)          # writes 512 MiB with a fill kernel
+            step()
+        torch.cuda.synchronize()
+        cold = op.profile_end()
+        del scratch
     ms_step = wall * 1e3 / args.steps
     tokens_per_s = w.tokens / (ms_step * 1e-3)
 
@@ -221,6 +243,14 @@ def main() -> int:
         kernels[name] = {"launches": n, "avg_us": avg * 1e3, "alg_bytes": b,
                          "gbps": b / (avg * 1e-3) / 1e9 if b else None,
                          "frac": b / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS if b else None}
+    cold_kernels = None
+    if cold is not None:
+        cold_kernels = {}
+        for name, (ms, n) in cold.items():
+            b = alg_bytes(name, w)
+            avg = ms / n
+            cold_kernels[name] = {"avg_us": avg * 1e3,
+                                  "frac": b / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS if b else None}
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
     dk = kernels[dom]
     # the method's bytes: x read once, K row copies written, K rows read back, one row
@@ -263,6 +293,9 @@ def main() -> int:
         "kernels": kernels,
         "ms_per_step_events": ms_step_events,
         "kernel_events": args.kernel_events,
+        "cold_cache": None if cold_kernels is None else {
+            "flush_mib": 512, "steps": args.cold_steps, "kernels": cold_kernels,
+            "kernel_sum_us": sum(v["avg_us"] for v in cold_kernels.values())},
     }
     parity = "skipped"
     result["cpu_baseline"] = None

@@ -28,6 +28,9 @@
  *    restrictions list).  Block sizes: 128 elements per fp32 scale for FP8,
  *    32 elements per E8M0 scale for MXFP4 (OCP Microscaling v1.0).
  *
+ *  - the rank-deduplicated dispatch and the standard-MoE conversion: see the
+ *    section of that name below.
+ *
  * Readings where the pages are silent are listed in the design notes; the ones
  * that shape this file: an expert index outside [0,E) gives its pair no row
  * (slot -1) and is counted; an all-zero FP8 block has scale 0 and codes 0x00;
@@ -311,6 +314,184 @@ void oracle_combine(int T, int H, int K, const int32_t *slot_of,
         }
     }
     free(w);
+}
+
+/* ---- rank-deduplicated dispatch and the standard-MoE conversion --------- */
+
+/*
+ * MORI names a "standard-MoE conversion" for its intra-node path ("Choosing
+ * an EP API and backend" page, "EP paths" table) and an intra-node kernel
+ * type ("Communication APIs" page, kernel types table) without defining
+ * either.  Reading used here: the dispatch sends each token once per
+ * destination rank that hosts at least one of its valid experts (a "unit"
+ * (t, r)); rank r's units are contiguous and ordered by token; the
+ * conversion then expands a rank's units into the expert-contiguous rows of
+ * the pair dispatch above, and on the way back sums the weighted expert
+ * outputs of each unit into one bf16 row that the combine adds up per token.
+ *
+ * Units: pair p = t*K + k with a valid expert e belongs to rank e / (E/R); the
+ * pair with the smallest k among the token's pairs on that rank opens the
+ * unit.  unit_cnt[R], unit_off[R+1] (exclusive scan), unit_of[T*K] (the unit
+ * row of each pair, -1 for an invalid expert) and unit_src[U] (the token of
+ * each unit row).  Returns U, or -1 on bad arguments.
+ */
+int oracle_route_units(int T, int K, int E, int R, const int32_t *indices,
+                       int32_t *unit_cnt, int32_t *unit_off, int32_t *unit_of,
+                       int32_t *unit_src)
+{
+    if (T < 0 || K <= 0 || E <= 0 || R <= 0 || E % R != 0)
+        return -1;
+    const int per_rank = E / R;
+    int32_t *open = (int32_t *)malloc(sizeof(int32_t) * (size_t)R);
+    int32_t *cursor = (int32_t *)malloc(sizeof(int32_t) * (size_t)R);
+    if (!open || !cursor) {
+        free(open);
+        free(cursor);
+        return -1;
+    }
+
+    /* count: one unit per (token, rank) that any valid pair of the token hits */
+    for (int r = 0; r < R; ++r)
+        unit_cnt[r] = 0;
+    for (int t = 0; t < T; ++t) {
+        for (int r = 0; r < R; ++r)
+            open[r] = 0;
+        for (int k = 0; k < K; ++k) {
+            int32_t e = indices[(long)t * K + k];
+            if (e < 0 || e >= E)
+                continue;
+            int r = e / per_rank;
+            if (!open[r]) {
+                open[r] = 1;
+                ++unit_cnt[r];
+            }
+        }
+    }
+    unit_off[0] = 0;
+    for (int r = 0; r < R; ++r)
+        unit_off[r + 1] = unit_off[r] + unit_cnt[r];
+
+    /* place: tokens in ascending order take the next row of each rank they hit */
+    for (int r = 0; r < R; ++r)
+        cursor[r] = unit_off[r];
+    for (int t = 0; t < T; ++t) {
+        for (int r = 0; r < R; ++r)
+            open[r] = -1;
+        for (int k = 0; k < K; ++k) {
+            long p = (long)t * K + k;
+            int32_t e = indices[p];
+            if (e < 0 || e >= E) {
+                unit_of[p] = -1;
+                continue;
+            }
+            int r = e / per_rank;
+            if (open[r] < 0) {
+                open[r] = cursor[r]++;
+                unit_src[open[r]] = t;
+            }
+            unit_of[p] = open[r];
+        }
+    }
+    int U = unit_off[R];
+    free(open);
+    free(cursor);
+    return U;
+}
+
+/* dst[u] = src[unit_src[u]] for u < U: each token's row, once per unit. */
+void oracle_gather_rows(int U, const int32_t *unit_src, const uint8_t *src,
+                        long row_bytes, uint8_t *dst)
+{
+    for (int u = 0; u < U; ++u)
+        memcpy(dst + (long)u * row_bytes, src + (long)unit_src[u] * row_bytes,
+               (size_t)row_bytes);
+}
+
+/* Standard-MoE conversion, dispatch direction: dst[slot_of[p]] =
+ * src[unit_of[p]] for every valid pair (a unit row goes to each of its
+ * expert rows). */
+void oracle_units_to_experts(long n_pairs, const int32_t *slot_of, const int32_t *unit_of,
+                             const uint8_t *src, long row_bytes, uint8_t *dst)
+{
+    for (long p = 0; p < n_pairs; ++p) {
+        if (slot_of[p] < 0 || unit_of[p] < 0)
+            continue;
+        memcpy(dst + (long)slot_of[p] * row_bytes, src + (long)unit_of[p] * row_bytes,
+               (size_t)row_bytes);
+    }
+}
+
+/*
+ * Standard-MoE conversion, combine direction: for unit u of token t,
+ * partial[u] = bf16_rne(sum over k = 0..K-1 with unit_of[t*K+k] == u of
+ * w(t,k) * in[slot_of[t*K+k]]), fp32 separate multiply and add from +0.0f;
+ * w(t,k) = weights[slot][k] with slot = slot_of[t*K+k], or 1 when weights is
+ * NULL (the weighting of B1's combine, applied on the expert side).
+ */
+void oracle_experts_to_units(int U, int H, int K, const int32_t *unit_src,
+                             const int32_t *unit_of, const int32_t *slot_of,
+                             const uint16_t *in, const float *weights, uint16_t *partial)
+{
+    for (int u = 0; u < U; ++u) {
+        long t = unit_src[u];
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                long p = t * K + k;
+                int32_t s = slot_of[p];
+                if (unit_of[p] != u || s < 0)
+                    continue;
+                float w = weights ? weights[(long)s * K + k] : 1.0f;
+                float prod = w * bf16_to_f32(in[(long)s * H + h]);
+                acc = acc + prod;
+            }
+            partial[(long)u * H + h] = f32_to_bf16_rne(acc);
+        }
+    }
+}
+
+/*
+ * Combine of unit rows: out[t] = bf16_rne(sum of f32(partial[u]) over the
+ * token's distinct units in ascending row order, i.e. ascending rank), from
+ * +0.0f; +0 for a token with no unit.  out_weights[t][k] =
+ * unit_weights[unit_of[t*K+k]][k] (1 when unit_weights is NULL), 0 for a pair
+ * with no unit.
+ */
+void oracle_combine_units(int T, int H, int K, const int32_t *unit_of,
+                          const uint16_t *partial, const float *unit_weights,
+                          uint16_t *out, float *out_weights)
+{
+    int32_t *units = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
+    for (int t = 0; t < T; ++t) {
+        /* the token's distinct units, ascending (insertion sort of <= K ids) */
+        int n = 0;
+        for (int k = 0; k < K; ++k) {
+            long p = (long)t * K + k;
+            int32_t u = unit_of[p];
+            if (out_weights)
+                out_weights[p] = u < 0 ? 0.0f : (unit_weights ? unit_weights[(long)u * K + k] : 1.0f);
+            if (u < 0)
+                continue;
+            int seen = 0;
+            for (int i = 0; i < n; ++i)
+                seen |= units[i] == u;
+            if (seen)
+                continue;
+            int i = n++;
+            while (i > 0 && units[i - 1] > u) {
+                units[i] = units[i - 1];
+                --i;
+            }
+            units[i] = u;
+        }
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int i = 0; i < n; ++i)
+                acc = acc + bf16_to_f32(partial[(long)units[i] * H + h]);
+            out[(long)t * H + h] = f32_to_bf16_rne(acc);
+        }
+    }
+    free(units);
 }
 
 /* Exposed for the oracle's own pins (bf16 rounding). */

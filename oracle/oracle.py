@@ -58,6 +58,12 @@ def _load():
     lib.oracle_quant_mxfp4.restype = I
     lib.oracle_combine.argtypes = [I, I, I, P, P, P, P, P]
     lib.oracle_combine.restype = None
+    lib.oracle_route_units.argtypes = [I, I, I, I, P, P, P, P, P]
+    lib.oracle_route_units.restype = I
+    lib.oracle_gather_rows.argtypes = [I, P, P, L, P]
+    lib.oracle_units_to_experts.argtypes = [L, P, P, P, L, P]
+    lib.oracle_experts_to_units.argtypes = [I, I, I, P, P, P, P, P, P]
+    lib.oracle_combine_units.argtypes = [I, I, I, P, P, P, P, P]
     lib.oracle_e4m3_encode_array.argtypes = [L, P, P]
     lib.oracle_e2m1_encode_array.argtypes = [L, P, P]
     lib.oracle_f32_to_bf16_array.argtypes = [L, P, P]
@@ -207,4 +213,102 @@ def combine(inp: np.ndarray, weights: Optional[np.ndarray], slot_of: np.ndarray,
     out_w = np.empty((tokens, topk), np.float32)
     _load().oracle_combine(int(tokens), H, int(topk), _ptr(so), _ptr(x), _ptr(w),
                            _ptr(out), _ptr(out_w))
+    return out, out_w
+
+
+# ---- rank-deduplicated dispatch and the standard-MoE conversion ------------------
+
+def route_units(indices: np.ndarray, num_experts: int, num_ranks: int) -> Dict[str, np.ndarray]:
+    """One unit per (token, destination rank): unit_cnt [R] (rows per rank),
+    unit_off [R+1], unit_of [T*K] (-1 for an invalid expert), unit_src [U]."""
+    idx = _c(indices, np.int32)
+    T, K = idx.shape
+    R = int(num_ranks)
+    cnt = np.zeros(R, np.int32)
+    off = np.zeros(R + 1, np.int32)
+    unit_of = np.zeros(T * K, np.int32)
+    src = np.zeros(T * min(K, R), np.int32)
+    U = _load().oracle_route_units(T, K, int(num_experts), R, _ptr(idx), _ptr(cnt), _ptr(off),
+                                   _ptr(unit_of), _ptr(src))
+    if U < 0:
+        raise ValueError("oracle_route_units: bad arguments")
+    return {"unit_cnt": cnt, "unit_off": off, "unit_of": unit_of, "unit_src": src[:U].copy(),
+            "units": U}
+
+
+def gather_rows(src_rows: np.ndarray, unit_src: np.ndarray) -> np.ndarray:
+    """dst[u] = src_rows[unit_src[u]]."""
+    src = np.ascontiguousarray(src_rows)
+    T = src.shape[0]
+    row_bytes = src.nbytes // T if T else src.itemsize
+    us = _c(unit_src, np.int32)
+    dst = np.zeros((us.size,) + src.shape[1:], dtype=src.dtype)
+    _load().oracle_gather_rows(us.size, _ptr(us), _ptr(src), row_bytes, _ptr(dst))
+    return dst
+
+
+def dispatch_dedup(x: np.ndarray, weights: Optional[np.ndarray], indices: np.ndarray,
+                   num_experts: int, num_ranks: int, quant: str = "none",
+                   scales: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Reference rank-deduplicated dispatch: the token's row (quantized once
+    per token when asked) and its weights/scales/indices rows, once per unit.
+    Also returns the pair routing (``slot_of`` ...) the conversion uses."""
+    idx = _c(indices, np.int32)
+    out = dict(route(idx, num_experts, num_ranks))
+    u = route_units(idx, num_experts, num_ranks)
+    out.update(u)
+    if quant == "none":
+        payload, sc = x, scales
+    elif quant == "fp8_e4m3_b128":
+        payload, sc = quant_fp8(x)
+    elif quant == "mxfp4_b32":
+        payload, sc = quant_mxfp4(x)
+    else:
+        raise ValueError(quant)
+    us = u["unit_src"]
+    out["recv_count"] = u["unit_cnt"]
+    out["out"] = gather_rows(payload, us)
+    out["out_indices"] = gather_rows(idx, us)
+    out["out_weights"] = None if weights is None else gather_rows(_c(weights, np.float32), us)
+    out["out_scales"] = None if sc is None else gather_rows(sc, us)
+    return out
+
+
+def units_to_experts(unit_rows: np.ndarray, slot_of: np.ndarray, unit_of: np.ndarray,
+                     n_rows: int) -> np.ndarray:
+    """Standard-MoE conversion of unit rows [U, ...] into expert-layout rows [n_rows, ...]."""
+    src = np.ascontiguousarray(unit_rows)
+    U = src.shape[0]
+    row_bytes = src.nbytes // U if U else src.itemsize
+    so = _c(slot_of, np.int32)
+    uo = _c(unit_of, np.int32)
+    dst = np.zeros((n_rows,) + src.shape[1:], dtype=src.dtype)
+    _load().oracle_units_to_experts(so.size, _ptr(so), _ptr(uo), _ptr(src), row_bytes, _ptr(dst))
+    return dst
+
+
+def experts_to_units(inp: np.ndarray, weights: Optional[np.ndarray], unit_src: np.ndarray,
+                     unit_of: np.ndarray, slot_of: np.ndarray, topk: int) -> np.ndarray:
+    """Weighted sum of each unit's expert rows: bf16 bits [N,H] -> bf16 bits [U,H]."""
+    x = _c(inp, np.uint16)
+    H = x.shape[1]
+    us = _c(unit_src, np.int32)
+    w = None if weights is None else _c(weights, np.float32)
+    out = np.empty((us.size, H), np.uint16)
+    _load().oracle_experts_to_units(us.size, H, int(topk), _ptr(us), _ptr(_c(unit_of, np.int32)),
+                                    _ptr(_c(slot_of, np.int32)), _ptr(x), _ptr(w), _ptr(out))
+    return out
+
+
+def combine_units(partial: np.ndarray, unit_weights: Optional[np.ndarray], unit_of: np.ndarray,
+                  tokens: int, topk: int):
+    """Sum of each token's unit rows (ascending rank): bf16 bits [U,H] ->
+    (bf16 bits [T,H], fp32 [T,K] weights read back from the unit rows)."""
+    x = _c(partial, np.uint16)
+    H = x.shape[1]
+    w = None if unit_weights is None else _c(unit_weights, np.float32)
+    out = np.empty((tokens, H), np.uint16)
+    out_w = np.empty((tokens, topk), np.float32)
+    _load().oracle_combine_units(int(tokens), H, int(topk), _ptr(_c(unit_of, np.int32)), _ptr(x),
+                                 _ptr(w), _ptr(out), _ptr(out_w))
     return out, out_w
