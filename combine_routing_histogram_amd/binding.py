@@ -37,7 +37,10 @@ EPDC_KERNEL_SCATTER = 2
 EPDC_KERNEL_SCATTER_FP8 = 3
 EPDC_KERNEL_SCATTER_MXFP4 = 4
 EPDC_KERNEL_COMBINE = 5
-EPDC_NUM_KERNELS = 6
+EPDC_KERNEL_UNITS_TO_EXPERTS = 6
+EPDC_KERNEL_EXPERTS_TO_UNITS = 7
+EPDC_KERNEL_COMBINE_UNITS = 8
+EPDC_NUM_KERNELS = 9
 
 
 class epdc_config(ctypes.Structure):
@@ -74,6 +77,11 @@ _SIGNATURES = {
     "epdc_combine_recv": (I32, [P, P]),
     "epdc_get_dispatch_src_token_pos": (I32, [P, ctypes.POINTER(P), PI32]),
     "epdc_get_routing": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P)]),
+    "epdc_dispatch_dedup": (I32, [P, P, I32, P, P, P, P, P, P, P, P, P]),
+    "epdc_get_unit_routing": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P)]),
+    "epdc_units_to_experts": (I32, [P, P, P, P, P, P, P, P, P, P]),
+    "epdc_experts_to_units": (I32, [P, P, P, P, P]),
+    "epdc_combine_units": (I32, [P, P, P, P, P, P]),
     "epdc_get_device_error": (I32, [P, P, PI32]),
     "epdc_reset": (I32, [P]),
     "epdc_last_error": (ctypes.c_char_p, []),
@@ -200,6 +208,41 @@ def epdc_get_routing(op: int) -> Tuple[int, int, int]:
     a, b, c = P(None), P(None), P(None)
     _check(lib().epdc_get_routing(op, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
     return a.value, b.value, c.value
+
+
+def epdc_dispatch_dedup(op: int, stream: int, num_tokens: int, input: int, weights: int,
+                        scales: int, indices: int, out: int, out_weights: int, out_scales: int,
+                        out_indices: int, recv_count: int) -> None:
+    _check(lib().epdc_dispatch_dedup(op, stream or None, num_tokens, input or None,
+                                     weights or None, scales or None, indices or None,
+                                     out or None, out_weights or None, out_scales or None,
+                                     out_indices or None, recv_count or None))
+
+
+def epdc_get_unit_routing(op: int) -> Tuple[int, int, int]:
+    a, b, c = P(None), P(None), P(None)
+    _check(lib().epdc_get_unit_routing(op, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def epdc_units_to_experts(op: int, stream: int, input: int, in_weights: int, in_scales: int,
+                          in_indices: int, out: int, out_weights: int, out_scales: int,
+                          out_indices: int) -> None:
+    _check(lib().epdc_units_to_experts(op, stream or None, input or None, in_weights or None,
+                                       in_scales or None, in_indices or None, out or None,
+                                       out_weights or None, out_scales or None,
+                                       out_indices or None))
+
+
+def epdc_experts_to_units(op: int, stream: int, input: int, weights: int, output: int) -> None:
+    _check(lib().epdc_experts_to_units(op, stream or None, input or None, weights or None,
+                                       output or None))
+
+
+def epdc_combine_units(op: int, stream: int, input: int, unit_weights: int, output: int,
+                       out_weights: int) -> None:
+    _check(lib().epdc_combine_units(op, stream or None, input or None, unit_weights or None,
+                                    output or None, out_weights or None))
 
 
 def epdc_get_device_error(op: int, stream: int) -> int:

@@ -45,10 +45,16 @@ bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 // Device workspace: control words, routing tables and the per-pair arrays.
 struct Layout {
-    size_t ctrl, tile_table, rank_in_tile, expert_off, rank_off, slot_of, src_pos, total;
+    size_t ctrl, tile_table, rank_in_tile, expert_off, rank_off, slot_of, src_pos;
+    // rank-deduplicated dispatch: the unit routing and the pairs' rank counts
+    size_t unit_table, unit_rank_in_tile, unit_off, unit_of, unit_src, pair_recv;
+    size_t total;
     int64_t n_cap;
+    int64_t u_cap;  // max_tokens * min(topk, num_ranks)
     int64_t tiles_max;
 };
+
+int units_per_token(const epdc_config &c) { return c.topk < c.num_ranks ? c.topk : c.num_ranks; }
 
 epdc_status check_config(const epdc_config *c)
 {
@@ -115,6 +121,19 @@ Layout layout_for(const epdc_config &c)
     off += align256(sizeof(int32_t) * (size_t)l.n_cap);
     l.src_pos = off;
     off += align256(sizeof(int32_t) * (size_t)l.n_cap);
+    l.u_cap = (int64_t)c.max_tokens * units_per_token(c);
+    l.unit_table = off;
+    off += align256(sizeof(int32_t) * (size_t)l.tiles_max * c.num_ranks);
+    l.unit_rank_in_tile = off;
+    off += align256(sizeof(int32_t) * (size_t)l.n_cap);
+    l.unit_off = off;
+    off += align256(sizeof(int32_t) * (size_t)(c.num_ranks + 1));
+    l.unit_of = off;
+    off += align256(sizeof(int32_t) * (size_t)l.n_cap);
+    l.unit_src = off;
+    off += align256(sizeof(int32_t) * (size_t)l.u_cap);
+    l.pair_recv = off;
+    off += align256(sizeof(int32_t) * (size_t)c.num_ranks);
     l.total = off;
     return l;
 }
@@ -139,7 +158,7 @@ void row_bytes_for(const epdc_config &c, size_t *payload, size_t *scales)
 
 const char *const kKernelNames[EPDC_NUM_KERNELS] = {
     "k_route_rank", "k_route_scan", "k_scatter_copy", "k_scatter_fp8", "k_scatter_mxfp4",
-    "k_combine"};
+    "k_combine", "k_units_to_experts", "k_experts_to_units", "k_combine_units"};
 
 }  // namespace
 
@@ -149,7 +168,9 @@ struct epdc_op {
     uint8_t *ws;
     Layout lay;
     int key_bits;
+    int unit_key_bits;
     bool routed;
+    bool units_routed;  // the last dispatch was rank-deduplicated
     int32_t last_tokens;
     // split-phase completion markers (timing disabled)
     hipEvent_t ev_dispatch, ev_combine;
@@ -249,8 +270,9 @@ epdc_status launch_scatter(epdc_op *op, hipStream_t st, ScatterArgs &sa, int mod
     const epdc_config &c = op->cfg;
     const int num_tokens = sa.num_tokens;
     const bool inline_route = mode == kRouteInline;
-    const int in_vecs = c.quant == EPDC_QUANT_NONE ? sa.in_row_vecs : c.hidden / 8;
-    const ScatterPlan plan = plan_scatter(c.quant, num_tokens, in_vecs, inline_route);
+    const int quant = mode == kRouteConvert ? (int)EPDC_QUANT_NONE : c.quant;
+    const int in_vecs = quant == EPDC_QUANT_NONE ? sa.in_row_vecs : c.hidden / 8;
+    const ScatterPlan plan = plan_scatter(quant, num_tokens, in_vecs, inline_route);
     sa.segs = plan.segs;
     sa.seg_vecs = plan.seg_vecs;
     int grid, block;
@@ -268,45 +290,102 @@ epdc_status launch_scatter(epdc_op *op, hipStream_t st, ScatterArgs &sa, int mod
             return s;
         sa.work_waves = block / kWave;
     }
+    if (mode == kRouteConvert)  // unit rows to expert rows: bytes, whatever the payload
+        return launch(op, st, EPDC_KERNEL_UNITS_TO_EXPERTS, [&] {
+            if (plan.ch == 8)
+                k_scatter_copy<8, kRouteConvert><<<grid, block, 0, st>>>(sa);
+            else
+                k_scatter_copy<2, kRouteConvert><<<grid, block, 0, st>>>(sa);
+        });
     switch (c.quant) {
     case EPDC_QUANT_FP8_E4M3_B128:
         return launch(op, st, EPDC_KERNEL_SCATTER_FP8, [&] {
-            if (mode == kRouteInline)
-                k_scatter_fp8<1, kRouteInline><<<grid, block, 0, st>>>(sa);
-            else if (mode == kRouteReplay)
-                k_scatter_fp8<1, kRouteReplay><<<grid, block, 0, st>>>(sa);
-            else
-                k_scatter_fp8<1><<<grid, block, 0, st>>>(sa);
+            switch (mode) {
+            case kRouteInline: k_scatter_fp8<1, kRouteInline><<<grid, block, 0, st>>>(sa); break;
+            case kRouteReplay: k_scatter_fp8<1, kRouteReplay><<<grid, block, 0, st>>>(sa); break;
+            case kRouteUnits: k_scatter_fp8<1, kRouteUnits><<<grid, block, 0, st>>>(sa); break;
+            case kRouteUnitsReplay:
+                k_scatter_fp8<1, kRouteUnitsReplay><<<grid, block, 0, st>>>(sa);
+                break;
+            default: k_scatter_fp8<1><<<grid, block, 0, st>>>(sa); break;
+            }
         });
     case EPDC_QUANT_MXFP4_B32:
         return launch(op, st, EPDC_KERNEL_SCATTER_MXFP4, [&] {
-            if (mode == kRouteInline)
-                k_scatter_mxfp4<2, kRouteInline><<<grid, block, 0, st>>>(sa);
-            else if (mode == kRouteReplay)
-                k_scatter_mxfp4<2, kRouteReplay><<<grid, block, 0, st>>>(sa);
-            else
-                k_scatter_mxfp4<2><<<grid, block, 0, st>>>(sa);
+            switch (mode) {
+            case kRouteInline: k_scatter_mxfp4<2, kRouteInline><<<grid, block, 0, st>>>(sa); break;
+            case kRouteReplay: k_scatter_mxfp4<2, kRouteReplay><<<grid, block, 0, st>>>(sa); break;
+            case kRouteUnits: k_scatter_mxfp4<2, kRouteUnits><<<grid, block, 0, st>>>(sa); break;
+            case kRouteUnitsReplay:
+                k_scatter_mxfp4<2, kRouteUnitsReplay><<<grid, block, 0, st>>>(sa);
+                break;
+            default: k_scatter_mxfp4<2><<<grid, block, 0, st>>>(sa); break;
+            }
         });
     default:
         return launch(op, st, EPDC_KERNEL_SCATTER, [&] {
-            if (mode == kRouteInline)
-                k_scatter_copy<2, kRouteInline><<<grid, block, 0, st>>>(sa);
-            else if (plan.ch == 8 && mode == kRouteReplay)
-                k_scatter_copy<8, kRouteReplay><<<grid, block, 0, st>>>(sa);
-            else if (mode == kRouteReplay)
-                k_scatter_copy<2, kRouteReplay><<<grid, block, 0, st>>>(sa);
-            else if (plan.ch == 8)
-                k_scatter_copy<8><<<grid, block, 0, st>>>(sa);
-            else
-                k_scatter_copy<2><<<grid, block, 0, st>>>(sa);
+            const bool wide = plan.ch == 8;
+            switch (mode) {
+            case kRouteInline: k_scatter_copy<2, kRouteInline><<<grid, block, 0, st>>>(sa); break;
+            case kRouteReplay:
+                if (wide)
+                    k_scatter_copy<8, kRouteReplay><<<grid, block, 0, st>>>(sa);
+                else
+                    k_scatter_copy<2, kRouteReplay><<<grid, block, 0, st>>>(sa);
+                break;
+            case kRouteUnits:
+                if (wide)
+                    k_scatter_copy<8, kRouteUnits><<<grid, block, 0, st>>>(sa);
+                else
+                    k_scatter_copy<2, kRouteUnits><<<grid, block, 0, st>>>(sa);
+                break;
+            case kRouteUnitsReplay:
+                if (wide)
+                    k_scatter_copy<8, kRouteUnitsReplay><<<grid, block, 0, st>>>(sa);
+                else
+                    k_scatter_copy<2, kRouteUnitsReplay><<<grid, block, 0, st>>>(sa);
+                break;
+            default:
+                if (wide)
+                    k_scatter_copy<8><<<grid, block, 0, st>>>(sa);
+                else
+                    k_scatter_copy<2><<<grid, block, 0, st>>>(sa);
+                break;
+            }
         });
     }
 }
 
-template <int KT>
+template <int KT, int MODE>
 void launch_combine(int grid, int block, hipStream_t st, const CombineArgs &a)
 {
-    k_combine<KT><<<grid, block, 0, st>>>(a);
+    k_combine<KT, kCombineSeg, MODE><<<grid, block, 0, st>>>(a);
+}
+
+// One wave per (row, 2 KiB segment) over `rows` output rows.
+template <int MODE>
+epdc_status launch_combine_mode(epdc_op *op, hipStream_t st, int kernel_id, CombineArgs &ca,
+                                int64_t rows)
+{
+    const epdc_config &c = op->cfg;
+    ca.topk = c.topk;
+    ca.row_vecs = c.hidden / 8;
+    ca.segs = (ca.row_vecs + kCombineSegVecs - 1) / kCombineSegVecs;
+    ca.num_tokens = (int32_t)rows;
+    int grid, block;
+    epdc_status s = grid_for_waves(rows * ca.segs, &grid, &block);
+    if (s != EPDC_SUCCESS)
+        return s;
+    return launch(op, st, kernel_id, [&] {
+        switch (c.topk) {
+        case 1: launch_combine<1, MODE>(grid, block, st, ca); break;
+        case 2: launch_combine<2, MODE>(grid, block, st, ca); break;
+        case 4: launch_combine<4, MODE>(grid, block, st, ca); break;
+        case 6: launch_combine<6, MODE>(grid, block, st, ca); break;
+        case 8: launch_combine<8, MODE>(grid, block, st, ca); break;
+        default: launch_combine<0, MODE>(grid, block, st, ca); break;
+        }
+    });
 }
 
 }  // namespace
@@ -389,7 +468,12 @@ epdc_status epdc_create(const epdc_config *cfg, void *workspace, size_t workspac
     while ((1 << bits) < cfg->num_experts)
         ++bits;
     o->key_bits = bits;
+    bits = 0;
+    while ((1 << bits) < cfg->num_ranks)
+        ++bits;
+    o->unit_key_bits = bits;
     o->routed = false;
+    o->units_routed = false;
     o->last_tokens = 0;
     o->profiling = false;
     o->ev_cap = o->ev_used = 0;
@@ -409,10 +493,15 @@ epdc_status epdc_destroy(epdc_op *op)
     return ok();
 }
 
-epdc_status epdc_dispatch(epdc_op *op, void *stream, int32_t num_tokens, const void *input,
+}  // extern "C"
+
+namespace {
+
+// Pair dispatch (dedup = false) or rank-deduplicated dispatch (dedup = true).
+epdc_status dispatch_impl(epdc_op *op, void *stream, int32_t num_tokens, const void *input,
                           const float *weights, const void *scales, const int32_t *indices,
                           void *out, float *out_weights, void *out_scales, int32_t *out_indices,
-                          int32_t *recv_count)
+                          int32_t *recv_count, bool dedup)
 {
     if (!op)
         return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
@@ -453,47 +542,79 @@ epdc_status epdc_dispatch(epdc_op *op, void *stream, int32_t num_tokens, const v
     const int n_pairs = num_tokens * c.topk;
     const int tiles = n_pairs > 0 ? (n_pairs + kRouteTile - 1) / kRouteTile : 1;
 
-    RouteArgs ra;
+    RouteArgs ra = {};
     ra.indices = indices;
     ra.n_pairs = n_pairs;
     ra.num_experts = c.num_experts;
     ra.num_ranks = c.num_ranks;
     ra.key_bits = op->key_bits;
+    ra.topk = c.topk;
+    ra.key_div = 0;
     ra.tiles = tiles;
     ra.tile_table = op->i32(op->lay.tile_table);
     ra.rank_in_tile = op->i32(op->lay.rank_in_tile);
     ra.expert_off = op->i32(op->lay.expert_off);
     ra.rank_off = op->i32(op->lay.rank_off);
-    ra.recv_count = recv_count;
+    ra.recv_count = dedup ? op->i32(op->lay.pair_recv) : recv_count;
     ra.ctrl = op->ctrl();
     const size_t lds = sizeof(int32_t) * (size_t)route_lds_ints(c.num_experts);
-    // One tile with tokens: the scatter launch below routes by itself.
-    const bool inline_route = tiles == 1 && num_tokens > 0;
     epdc_status s = EPDC_SUCCESS;
-    if (inline_route) {
-        // no route launch
-    } else if (tiles == 1) {
-        s = launch(op, st, EPDC_KERNEL_ROUTE, [&] {
-            k_route_rank<true><<<1, kRouteThreads, lds, st>>>(ra);
-        });
+    bool inline_route = false;
+    if (dedup) {
+        // the unit level: keys = destination ranks of the pairs that open a
+        // unit; its offsets are both the expert and the rank offsets (one key
+        // per rank), and its counts are the caller's recv_count
+        RouteArgs rb = ra;
+        rb.num_experts = c.num_ranks;
+        rb.key_bits = op->unit_key_bits;
+        rb.key_div = c.num_experts / c.num_ranks;
+        rb.tile_table = op->i32(op->lay.unit_table);
+        rb.rank_in_tile = op->i32(op->lay.unit_rank_in_tile);
+        rb.expert_off = op->i32(op->lay.unit_off);
+        rb.rank_off = op->i32(op->lay.unit_off);
+        rb.recv_count = recv_count;
+        if (tiles == 1) {
+            s = launch(op, st, EPDC_KERNEL_ROUTE, [&] {
+                k_route_rank2<true><<<dim3(1, 2), kRouteThreads, lds, st>>>(ra, rb);
+            });
+        } else {
+            s = launch(op, st, EPDC_KERNEL_ROUTE, [&] {
+                k_route_rank2<false><<<dim3(tiles, 2), kRouteThreads, lds, st>>>(ra, rb);
+            });
+            if (s == EPDC_SUCCESS)
+                s = launch(op, st, EPDC_KERNEL_ROUTE_SCAN, [&] {
+                    k_route_scan2<<<dim3(1, 2), kRouteThreads, 0, st>>>(ra, rb);
+                });
+        }
     } else {
-        s = launch(op, st, EPDC_KERNEL_ROUTE, [&] {
-            k_route_rank<false><<<tiles, kRouteThreads, lds, st>>>(ra);
-        });
-        if (s == EPDC_SUCCESS)
-            s = launch(op, st, EPDC_KERNEL_ROUTE_SCAN,
-                       [&] { k_route_scan<<<1, kRouteThreads, 0, st>>>(ra); });
+        // One tile with tokens: the scatter launch below routes by itself.
+        inline_route = tiles == 1 && num_tokens > 0;
+        if (inline_route) {
+            // no route launch
+        } else if (tiles == 1) {
+            s = launch(op, st, EPDC_KERNEL_ROUTE, [&] {
+                k_route_rank<true><<<1, kRouteThreads, lds, st>>>(ra);
+            });
+        } else {
+            s = launch(op, st, EPDC_KERNEL_ROUTE, [&] {
+                k_route_rank<false><<<tiles, kRouteThreads, lds, st>>>(ra);
+            });
+            if (s == EPDC_SUCCESS)
+                s = launch(op, st, EPDC_KERNEL_ROUTE_SCAN,
+                           [&] { k_route_scan<<<1, kRouteThreads, 0, st>>>(ra); });
+        }
     }
     if (s != EPDC_SUCCESS)
         return s;
 
     if (num_tokens == 0) {
         op->routed = true;
+        op->units_routed = dedup;
         op->last_tokens = 0;
         return ok();
     }
 
-    ScatterArgs sa;
+    ScatterArgs sa = {};
     sa.num_tokens = num_tokens;
     sa.n_pairs = n_pairs;
     sa.topk = c.topk;
@@ -519,13 +640,181 @@ epdc_status epdc_dispatch(epdc_op *op, void *stream, int32_t num_tokens, const v
     sa.expert_off = ra.expert_off;
     sa.rank_off = ra.rank_off;
     sa.recv_count = recv_count;
+    if (dedup) {
+        sa.key_div = c.num_experts / c.num_ranks;
+        sa.unit_table = op->i32(op->lay.unit_table);
+        sa.unit_rank_in_tile = op->i32(op->lay.unit_rank_in_tile);
+        sa.unit_of = op->i32(op->lay.unit_of);
+        sa.unit_src = op->i32(op->lay.unit_src);
+        sa.unit_rows_max = num_tokens * units_per_token(c);
+    }
 
-    s = launch_scatter(op, st, sa, inline_route ? kRouteInline : kRouteTable);
+    s = launch_scatter(op, st, sa,
+                       dedup ? kRouteUnits : (inline_route ? kRouteInline : kRouteTable));
     if (s != EPDC_SUCCESS)
         return s;
     op->routed = true;
+    op->units_routed = dedup;
     op->last_tokens = num_tokens;
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+epdc_status epdc_dispatch(epdc_op *op, void *stream, int32_t num_tokens, const void *input,
+                          const float *weights, const void *scales, const int32_t *indices,
+                          void *out, float *out_weights, void *out_scales, int32_t *out_indices,
+                          int32_t *recv_count)
+{
+    return dispatch_impl(op, stream, num_tokens, input, weights, scales, indices, out,
+                         out_weights, out_scales, out_indices, recv_count, false);
+}
+
+epdc_status epdc_dispatch_dedup(epdc_op *op, void *stream, int32_t num_tokens, const void *input,
+                                const float *weights, const void *scales, const int32_t *indices,
+                                void *out, float *out_weights, void *out_scales,
+                                int32_t *out_indices, int32_t *recv_count)
+{
+    return dispatch_impl(op, stream, num_tokens, input, weights, scales, indices, out,
+                         out_weights, out_scales, out_indices, recv_count, true);
+}
+
+epdc_status epdc_get_unit_routing(epdc_op *op, const int32_t **unit_off, const int32_t **unit_of,
+                                  const int32_t **unit_src)
+{
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    if (!op->units_routed)
+        return fail(EPDC_ERR_BAD_STATE, "no rank-deduplicated dispatch recorded");
+    if (unit_off)
+        *unit_off = op->i32(op->lay.unit_off);
+    if (unit_of)
+        *unit_of = op->i32(op->lay.unit_of);
+    if (unit_src)
+        *unit_src = op->i32(op->lay.unit_src);
+    return ok();
+}
+
+epdc_status epdc_units_to_experts(epdc_op *op, void *stream, const void *input,
+                                  const float *in_weights, const void *in_scales,
+                                  const int32_t *in_indices, void *out, float *out_weights,
+                                  void *out_scales, int32_t *out_indices)
+{
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    if (!op->units_routed)
+        return fail(EPDC_ERR_BAD_STATE, "the conversion needs a rank-deduplicated dispatch first");
+    const epdc_config &c = op->cfg;
+    const int T = op->last_tokens;
+    if (T == 0)
+        return ok();
+    if (!input || !out)
+        return fail(EPDC_ERR_INVALID_ARGS, "input and out are required");
+    if ((in_weights == nullptr) != (out_weights == nullptr) ||
+        (in_scales == nullptr) != (out_scales == nullptr) ||
+        (in_indices == nullptr) != (out_indices == nullptr))
+        return fail(EPDC_ERR_INVALID_ARGS,
+                    "each carried array needs both its input and its output, or neither");
+    size_t payload, scale_bytes;
+    row_bytes_for(c, &payload, &scale_bytes);
+    if (in_scales && (scale_bytes == 0 || scale_bytes % 4 != 0))
+        return fail(EPDC_ERR_INVALID_ARGS,
+                    "scale rows of %zu bytes cannot be converted (need a positive multiple of 4)",
+                    scale_bytes);
+    if (!aligned(input, 16) || !aligned(out, 16) || !aligned(in_weights, 4) ||
+        !aligned(in_scales, 4) || !aligned(in_indices, 4) || !aligned(out_weights, 4) ||
+        !aligned(out_scales, 4) || !aligned(out_indices, 4))
+        return fail(EPDC_ERR_INVALID_ARGS,
+                    "input/out must be 16-byte aligned, the other arrays 4-byte aligned");
+
+    ScatterArgs sa = {};
+    sa.num_tokens = T * units_per_token(c);  // the grid covers the unit capacity
+    sa.row_count = op->i32(op->lay.unit_off) + c.num_ranks;
+    sa.n_pairs = T * c.topk;
+    sa.topk = c.topk;
+    sa.num_experts = c.num_experts;
+    sa.hidden = c.hidden;
+    sa.input = static_cast<const uint8_t *>(input);
+    sa.in_row_vecs = (int)(payload / 16);
+    sa.out = static_cast<uint8_t *>(out);
+    sa.weights = in_weights;
+    sa.out_weights = out_weights;
+    sa.indices = in_indices;
+    sa.out_indices = out_indices;
+    sa.scales = static_cast<const uint8_t *>(in_scales);
+    sa.out_scales = static_cast<uint8_t *>(out_scales);
+    sa.scale_words = in_scales ? (int)(scale_bytes / 4) : 0;
+    sa.slot_of = op->i32(op->lay.slot_of);
+    sa.unit_of = op->i32(op->lay.unit_of);
+    sa.unit_src = op->i32(op->lay.unit_src);
+    sa.num_src_tokens = T;
+    sa.num_ranks = c.num_ranks;
+    sa.ctrl = op->ctrl();
+    const epdc_status s = launch_scatter(op, static_cast<hipStream_t>(stream), sa, kRouteConvert);
+    return s == EPDC_SUCCESS ? ok() : s;
+}
+
+epdc_status epdc_experts_to_units(epdc_op *op, void *stream, const void *input,
+                                  const float *weights, void *output)
+{
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    if (!op->units_routed)
+        return fail(EPDC_ERR_BAD_STATE, "the conversion needs a rank-deduplicated dispatch first");
+    const epdc_config &c = op->cfg;
+    const int T = op->last_tokens;
+    if (T == 0)
+        return ok();
+    if (!input || !output)
+        return fail(EPDC_ERR_INVALID_ARGS, "input and output are required");
+    if (!aligned(input, 16) || !aligned(output, 16) || !aligned(weights, 4))
+        return fail(EPDC_ERR_INVALID_ARGS,
+                    "input/output must be 16-byte aligned, weights 4-byte aligned");
+    CombineArgs ca = {};
+    ca.slot_of = op->i32(op->lay.slot_of);
+    ca.input = static_cast<const uint8_t *>(input);
+    ca.weights = weights;
+    ca.output = static_cast<uint8_t *>(output);
+    ca.unit_of = op->i32(op->lay.unit_of);
+    ca.unit_src = op->i32(op->lay.unit_src);
+    ca.row_count = op->i32(op->lay.unit_off) + c.num_ranks;
+    ca.n_pairs = T * c.topk;
+    ca.num_src_tokens = T;
+    const epdc_status s = launch_combine_mode<kCombineUnitsIn>(
+        op, static_cast<hipStream_t>(stream), EPDC_KERNEL_EXPERTS_TO_UNITS, ca,
+        (int64_t)T * units_per_token(c));
+    return s == EPDC_SUCCESS ? ok() : s;
+}
+
+epdc_status epdc_combine_units(epdc_op *op, void *stream, const void *input,
+                               const float *unit_weights, void *output, float *out_weights)
+{
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    if (!op->units_routed)
+        return fail(EPDC_ERR_BAD_STATE, "combine_units needs a rank-deduplicated dispatch first");
+    const epdc_config &c = op->cfg;
+    const int T = op->last_tokens;
+    if (T == 0)
+        return ok();
+    if (!input || !output)
+        return fail(EPDC_ERR_INVALID_ARGS, "input and output are required");
+    if (!aligned(input, 16) || !aligned(output, 16) || !aligned(unit_weights, 4) ||
+        !aligned(out_weights, 4))
+        return fail(EPDC_ERR_INVALID_ARGS,
+                    "input/output must be 16-byte aligned, weights 4-byte aligned");
+    CombineArgs ca = {};
+    ca.input = static_cast<const uint8_t *>(input);
+    ca.weights = unit_weights;
+    ca.output = static_cast<uint8_t *>(output);
+    ca.out_weights = out_weights;
+    ca.unit_of = op->i32(op->lay.unit_of);
+    ca.in_rows_max = T * units_per_token(c);
+    const epdc_status s = launch_combine_mode<kCombineUnitsOut>(
+        op, static_cast<hipStream_t>(stream), EPDC_KERNEL_COMBINE_UNITS, ca, T);
+    return s == EPDC_SUCCESS ? ok() : s;
 }
 
 epdc_status epdc_combine(epdc_op *op, void *stream, const void *input, const float *weights,
@@ -547,35 +836,16 @@ epdc_status epdc_combine(epdc_op *op, void *stream, const void *input, const flo
         return fail(EPDC_ERR_INVALID_ARGS,
                     "input/output must be 16-byte aligned, weights 4-byte aligned");
 
-    CombineArgs ca;
-    ca.num_tokens = T;
-    ca.topk = c.topk;
-    ca.row_vecs = c.hidden / 8;
-    ca.segs = (ca.row_vecs + kCombineSegVecs - 1) / kCombineSegVecs;
+    CombineArgs ca = {};
     ca.slot_of = op->i32(op->lay.slot_of);
     ca.input = static_cast<const uint8_t *>(input);
     ca.weights = weights;
     ca.output = static_cast<uint8_t *>(output);
     ca.out_weights = out_weights;
-
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    int grid, block;  // one wave per (token, row segment)
-    epdc_status s = grid_for_waves((int64_t)T * ca.segs, &grid, &block);
-    if (s != EPDC_SUCCESS)
-        return s;
-    s = launch(op, st, EPDC_KERNEL_COMBINE, [&] {
-        switch (c.topk) {
-        case 1: launch_combine<1>(grid, block, st, ca); break;
-        case 2: launch_combine<2>(grid, block, st, ca); break;
-        case 4: launch_combine<4>(grid, block, st, ca); break;
-        case 6: launch_combine<6>(grid, block, st, ca); break;
-        case 8: launch_combine<8>(grid, block, st, ca); break;
-        default: launch_combine<0>(grid, block, st, ca); break;
-        }
-    });
-    if (s != EPDC_SUCCESS)
-        return s;
-    return ok();
+    (void)c;
+    const epdc_status s = launch_combine_mode<kCombinePairs>(
+        op, static_cast<hipStream_t>(stream), EPDC_KERNEL_COMBINE, ca, T);
+    return s == EPDC_SUCCESS ? ok() : s;
 }
 
 epdc_status epdc_dispatch_replay(epdc_op *op, void *stream, const void *input,
@@ -622,7 +892,13 @@ epdc_status epdc_dispatch_replay(epdc_op *op, void *stream, const void *input,
     sa.out_scales = static_cast<uint8_t *>(out_scales);
     sa.scale_words = c.scale_row_bytes / 4;
     sa.ctrl = op->ctrl();
-    epdc_status s = launch_scatter(op, static_cast<hipStream_t>(stream), sa, kRouteReplay);
+    int mode = kRouteReplay;
+    if (op->units_routed) {  // replay the unit rows of a rank-deduplicated dispatch
+        sa.unit_of = op->i32(op->lay.unit_of);
+        sa.unit_rows_max = T * units_per_token(c);
+        mode = kRouteUnitsReplay;
+    }
+    epdc_status s = launch_scatter(op, static_cast<hipStream_t>(stream), sa, mode);
     return s == EPDC_SUCCESS ? ok() : s;
 }
 
@@ -732,6 +1008,7 @@ epdc_status epdc_reset(epdc_op *op)
     if (!op)
         return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
     op->routed = false;
+    op->units_routed = false;
     op->last_tokens = 0;
     op->dispatch_sent = op->combine_sent = false;
     return ok();

@@ -93,7 +93,9 @@ struct RouteArgs {
     int32_t n_pairs;
     int32_t num_experts;
     int32_t num_ranks;
-    int32_t key_bits;        // bits that hold any expert id < num_experts
+    int32_t key_bits;        // bits that hold any key < num_experts
+    int32_t topk;            // pairs per token
+    int32_t key_div;         // 0: the key is the expert id; > 0: unit keys (below)
     int32_t tiles;           // ceil(n_pairs / kRouteTile), >= 1
     int32_t *tile_table;     // [tiles][E]: counts, then first slot per (tile, e)
     int32_t *rank_in_tile;   // [n_pairs], -1 for an invalid id
@@ -163,8 +165,39 @@ struct TileRank {
     int e, rank, col_total;
 };
 
+// Routing key of pair p, or -1 for no row.  key_div == 0: the expert id,
+// valid in [0, E).  key_div > 0 (units of the rank-deduplicated dispatch, E
+// = number of ranks, key_div = experts per rank): the pair's destination
+// rank id / key_div for the pair with the smallest k among the token's pairs
+// on that rank (it opens the unit), -1 for the token's other pairs there; ids
+// outside [0, key_div * E) have no key either way.
+__device__ inline int route_key(const int32_t *indices, int p, int E, int topk, int key_div,
+                                bool &bad_id)
+{
+    const int v = indices[p];
+    bad_id = false;
+    if (key_div == 0) {
+        if (v >= 0 && v < E)
+            return v;
+        bad_id = true;
+        return -1;
+    }
+    const int limit = key_div * E;
+    if (v < 0 || v >= limit)
+        return -1;
+    const int r = v / key_div;
+    const int k = p % topk;
+    for (int j = 1; j <= k; ++j) {
+        const int u = indices[p - j];
+        if (u >= 0 && u < limit && u / key_div == r)
+            return -1;
+    }
+    return r;
+}
+
 __device__ inline TileRank rank_tile(const int32_t *indices, int n_pairs, int E, int key_bits,
-                                     int p, int32_t *wave_cnt, uint32_t *ctrl, bool flag_errors)
+                                     int topk, int key_div, int p, int32_t *wave_cnt,
+                                     uint32_t *ctrl, bool flag_errors)
 {
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -173,10 +206,9 @@ __device__ inline TileRank rank_tile(const int32_t *indices, int n_pairs, int E,
 
     int e = -1;
     if (p < n_pairs) {
-        const int v = indices[p];
-        if (v >= 0 && v < E)
-            e = v;
-        else if (flag_errors)
+        bool bad_id;
+        e = route_key(indices, p, E, topk, key_div, bad_id);
+        if (bad_id && flag_errors)
             atomicOr(&ctrl[kCtrlError], 1u);
     }
     const bool valid = e >= 0;
@@ -219,7 +251,7 @@ __device__ inline TileRank rank_tile(const int32_t *indices, int n_pairs, int E,
 }
 
 template <bool SINGLE_TILE>
-__global__ __launch_bounds__(kRouteThreads) void k_route_rank(RouteArgs a)
+__device__ inline void route_rank_body(const RouteArgs &a)
 {
     extern __shared__ int32_t lds[];
     __shared__ int32_t s_wave_tot[kRouteWaves + 1];
@@ -231,7 +263,8 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_rank(RouteArgs a)
     int32_t *wave_cnt = lds;                     // [kRouteWaves][E]
     int32_t *eoff = lds + kRouteWaves * E;       // [E+1] (single tile)
 
-    const TileRank r = rank_tile(a.indices, a.n_pairs, E, a.key_bits, p, wave_cnt, a.ctrl, true);
+    const TileRank r = rank_tile(a.indices, a.n_pairs, E, a.key_bits, a.topk, a.key_div, p,
+                                 wave_cnt, a.ctrl, a.key_div == 0);
     if (p < a.n_pairs)
         a.rank_in_tile[p] = r.rank;
     if (!SINGLE_TILE) {
@@ -246,11 +279,25 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_rank(RouteArgs a)
     }
 }
 
+template <bool SINGLE_TILE>
+__global__ __launch_bounds__(kRouteThreads) void k_route_rank(RouteArgs a)
+{
+    route_rank_body<SINGLE_TILE>(a);
+}
+
+// Both routing levels of the rank-deduplicated dispatch in one launch:
+// blockIdx.y = 0 routes the pairs to experts, 1 the units to ranks.
+template <bool SINGLE_TILE>
+__global__ __launch_bounds__(kRouteThreads) void k_route_rank2(RouteArgs a, RouteArgs b)
+{
+    route_rank_body<SINGLE_TILE>(blockIdx.y == 0 ? a : b);
+}
+
 // One block.  Column chunks of up to kScanRegs tiles stay in registers
 // between the two passes; longer columns are re-read from memory.
 constexpr int kScanRegs = 16;
 
-__global__ __launch_bounds__(kRouteThreads) void k_route_scan(RouteArgs a)
+__device__ inline void route_scan_body(const RouteArgs &a)
 {
     __shared__ int32_t part[kRouteThreads];
     __shared__ int32_t eoff[kMaxExperts + 1];
@@ -319,6 +366,16 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scan(RouteArgs a)
     }
 }
 
+__global__ __launch_bounds__(kRouteThreads) void k_route_scan(RouteArgs a)
+{
+    route_scan_body(a);
+}
+
+__global__ __launch_bounds__(kRouteThreads) void k_route_scan2(RouteArgs a, RouteArgs b)
+{
+    route_scan_body(blockIdx.y == 0 ? a : b);
+}
+
 // ---------------------------------------------------------------------------
 // Dispatch scatter: one wave per (token, row segment)
 // ---------------------------------------------------------------------------
@@ -361,6 +418,16 @@ struct ScatterArgs {
     int32_t *expert_off;         // [E+1]
     int32_t *rank_off;           // [R+1]
     int32_t *recv_count;         // [R]
+    // rank-deduplicated dispatch ("units": one row per (token, rank)) and
+    // its conversion to the expert layout
+    int32_t key_div;                   // experts per rank
+    const int32_t *unit_table;         // [tiles][R]: first unit row per (tile, rank)
+    const int32_t *unit_rank_in_tile;  // [T*K]: rank among the tile's unit openers, or -1
+    int32_t *unit_of;                  // [T*K]: unit row of each pair, -1 for none
+    int32_t *unit_src;                 // [U_cap]: token of each unit row
+    const int32_t *row_count;          // device count of input rows (units), or NULL
+    int32_t unit_rows_max;             // num_tokens * min(K, R): every unit row is below
+    int32_t num_src_tokens;            // tokens of the recorded dispatch (conversion)
 };
 
 // ---- inline routing for a single tile (num_tokens * K <= kRouteTile) ----
@@ -385,7 +452,7 @@ __device__ inline void inline_route(const ScatterArgs &a, InlineRouteLds &l)
 {
     const int tid = threadIdx.x;
     const bool first = blockIdx.x == 0;
-    const TileRank r = rank_tile(a.indices, a.n_pairs, a.num_experts, a.key_bits, tid,
+    const TileRank r = rank_tile(a.indices, a.n_pairs, a.num_experts, a.key_bits, a.topk, 0, tid,
                                  l.wave_cnt, a.ctrl, first);
     write_offsets(a.num_experts, a.num_ranks, r.col_total, l.eoff, l.wave_tot, a.expert_off,
                   a.rank_off, a.recv_count, first);
@@ -487,6 +554,9 @@ __device__ inline bool scatter_wave_range(const ScatterArgs &a, int row_vecs, Sc
     const int wv = blockIdx.x * a.work_waves + wave;
     if (wv >= a.num_tokens * a.segs)
         return false;
+    // the grid covers the row capacity; rows past the device count have no work
+    if (a.row_count && wv / a.segs >= *a.row_count)
+        return false;
     w.t = wv / a.segs;
     seg = wv - w.t * a.segs;
     w.base = seg * a.seg_vecs;
@@ -504,8 +574,71 @@ __device__ inline InlineRouteLds &inline_route_lds()
 enum {
     kRouteTable = 0,   // the tile table of the two-launch route
     kRouteInline = 1,  // routes the single tile itself (kRouteThreads-thread blocks)
-    kRouteReplay = 2   // slot_of of a dispatch recorded earlier (routing replay)
+    kRouteReplay = 2,  // slot_of of a dispatch recorded earlier (routing replay)
+    kRouteUnits = 3,        // rank-deduplicated: one row per (token, rank), from the unit table
+    kRouteConvert = 4,      // a wave per unit row: its pairs' expert rows (standard-MoE layout)
+    kRouteUnitsReplay = 5   // unit rows of a rank-deduplicated dispatch recorded earlier
 };
+
+// Rank-deduplicated dispatch: the pair's expert slot is recorded as in
+// kRouteTable (the conversion and the combine use it), and the wave writes
+// the token's row once per unit: the unit opener (smallest k of the token on
+// that rank) holds the unit row, the token's other pairs on the rank take the
+// opener's row as their unit.
+__device__ inline int unit_slot(const ScatterArgs &a, int t, int lane, bool record)
+{
+    const int K = a.topk;
+    const int R = a.num_ranks;
+    int rank = -1, us = -1;
+    if (lane < K) {
+        const int p = t * K + lane;
+        const int v = a.indices[p];
+        if (v >= 0 && v < a.num_experts)
+            rank = v / a.key_div;
+        const int ur = a.unit_rank_in_tile[p];
+        if (ur >= 0 && rank >= 0) {
+            us = a.unit_table[(size_t)(p / kRouteTile) * R + rank] + ur;
+            if ((unsigned)us >= (unsigned)a.unit_rows_max) {
+                if (record)
+                    atomicOr(&a.ctrl[kCtrlError], 2u);
+                us = -1;
+            }
+        }
+    }
+    // the unit of every pair: the row of the opener on the same rank
+    int unit = -1;
+    for (int j = 0; j < K; ++j) {
+        const int rj = __shfl(rank, j, kWave);
+        const int uj = __shfl(us, j, kWave);
+        if (unit < 0 && rank >= 0 && rj == rank && uj >= 0)
+            unit = uj;
+    }
+    if (record && lane < K) {
+        a.unit_of[t * K + lane] = unit;
+        if (us >= 0)
+            a.unit_src[us] = t;
+    }
+    return us;
+}
+
+// Conversion of unit rows to the expert layout: the wave's row is unit u of
+// token unit_src[u]; lane k's slot is the expert row of pair k when that pair
+// belongs to u.
+__device__ inline int convert_slot(const ScatterArgs &a, int u, int lane)
+{
+    if (lane >= a.topk)
+        return -1;
+    const int t = a.unit_src[u];
+    if ((unsigned)t >= (unsigned)a.num_src_tokens) {
+        atomicOr(&a.ctrl[kCtrlError], 2u);
+        return -1;
+    }
+    const int p = t * a.topk + lane;
+    if (a.unit_of[p] != u)
+        return -1;
+    const int s = a.slot_of[p];
+    return (unsigned)s < (unsigned)a.n_pairs ? s : -1;
+}
 
 // The K slots of the wave's token (lane k holds pair k's slot), recorded by
 // the segment-0 wave, which also carries the small rows.  With kRouteInline
@@ -520,6 +653,31 @@ __device__ inline void route_wave(const ScatterArgs &a, bool has_work, int seg, 
         inline_route(a, l);
         if (has_work)
             w.slot = pair_slot_inline(a, l, w.t, w.lane, seg == 0);
+    } else if constexpr (MODE == kRouteUnits) {
+        if (has_work) {  // wave-uniform: the shuffles in unit_slot see the whole wave
+            if (seg == 0)
+                (void)pair_slot(a, w.t, w.lane, true);
+            w.slot = unit_slot(a, w.t, w.lane, seg == 0);
+        }
+    } else if constexpr (MODE == kRouteConvert) {
+        if (has_work)
+            w.slot = convert_slot(a, w.t, w.lane);
+    } else if constexpr (MODE == kRouteUnitsReplay) {
+        if (has_work) {  // wave-uniform
+            int u = -1;
+            if (w.lane < a.topk) {
+                u = a.unit_of[w.t * a.topk + w.lane];
+                if ((unsigned)u >= (unsigned)a.unit_rows_max)
+                    u = -1;
+            }
+            int opener = u >= 0;  // the first of the token's pairs in the unit writes it
+            for (int j = 0; j < a.topk; ++j) {
+                const int uj = __shfl(u, j, kWave);
+                if (j < w.lane && uj == u)
+                    opener = 0;
+            }
+            w.slot = opener ? u : -1;
+        }
     } else if constexpr (MODE == kRouteReplay) {
         if (has_work && w.lane < a.topk) {
             const int s = a.slot_of[w.t * a.topk + w.lane];
@@ -755,7 +913,86 @@ struct CombineArgs {
     const float *weights;    // [rows, K] or NULL
     uint8_t *output;         // [T, H] bf16
     float *out_weights;      // [T, K] or NULL
+    // unit modes (rank-deduplicated path)
+    const int32_t *unit_of;    // [T*K]
+    const int32_t *unit_src;   // [U_cap]
+    const int32_t *row_count;  // device count of output rows (units), or NULL
+    int32_t n_pairs;           // expert rows of the recorded dispatch
+    int32_t num_src_tokens;    // tokens of the recorded dispatch
+    int32_t in_rows_max;       // rows of the unit-row input
 };
+
+// What a combine wave sums.
+enum {
+    kCombinePairs = 0,     // token t: its K expert rows, weighted (the gather combine)
+    kCombineUnitsIn = 1,   // unit u: the expert rows of its pairs, weighted
+    kCombineUnitsOut = 2   // token t: its distinct unit rows in ascending order, unweighted
+};
+
+// Lane k's (row, weight) term of the wave's sum, k = 0..K-1 in summation
+// order (-1: none); also writes the returned weights where the mode has them.
+template <int MODE>
+__device__ inline void combine_terms(const CombineArgs &a, int row, int sg, int lane, int K,
+                                     int &my_slot, float &my_w)
+{
+    my_slot = -1;
+    my_w = 0.0f;
+    if constexpr (MODE == kCombinePairs) {
+        if (lane < K) {
+            const int p = row * K + lane;
+            my_slot = a.slot_of[p];
+            if (my_slot >= 0)
+                my_w = a.weights ? a.weights[(size_t)my_slot * K + lane] : 1.0f;
+            if (a.out_weights && sg == 0)
+                a.out_weights[p] = my_w;
+        }
+    } else if constexpr (MODE == kCombineUnitsIn) {
+        if (lane < K) {
+            const int t = a.unit_src[row];
+            if ((unsigned)t < (unsigned)a.num_src_tokens) {
+                const int p = t * K + lane;
+                const int s = a.slot_of[p];
+                if (a.unit_of[p] == row && (unsigned)s < (unsigned)a.n_pairs) {
+                    my_slot = s;
+                    my_w = a.weights ? a.weights[(size_t)s * K + lane] : 1.0f;
+                }
+            }
+        }
+    } else {
+        int u = -1;
+        if (lane < K) {
+            u = a.unit_of[row * K + lane];
+            if ((unsigned)u >= (unsigned)a.in_rows_max)
+                u = -1;
+            if (a.out_weights && sg == 0)
+                a.out_weights[row * K + lane] =
+                    u < 0 ? 0.0f : (a.weights ? a.weights[(size_t)u * K + lane] : 1.0f);
+        }
+        // the first lane holding a unit opens it; openers are ordered by unit row
+        int opener = u >= 0;
+        for (int j = 0; j < K; ++j) {
+            const int uj = __shfl(u, j, kWave);
+            if (j < lane && uj == u)
+                opener = 0;
+        }
+        int pos = 0;
+        for (int j = 0; j < K; ++j) {
+            const int uj = __shfl(u, j, kWave);
+            const int oj = __shfl(opener, j, kWave);
+            if (oj && uj < u)
+                ++pos;
+        }
+        for (int j = 0; j < K; ++j) {
+            const int uj = __shfl(u, j, kWave);
+            const int oj = __shfl(opener, j, kWave);
+            const int pj = __shfl(pos, j, kWave);
+            if (oj && pj == lane) {
+                my_slot = uj;
+                my_w = 1.0f;  // 1 * x is x: the sum is that of the unit rows
+            }
+        }
+    }
+}
 
 __device__ inline uint32_t pack_bf16_rne(float lo, float hi)
 {
@@ -778,27 +1015,22 @@ __device__ inline void accumulate_row(float *acc, float w, u32x4 x)
 
 // KT = K known at compile time (double-buffered), or 0: runtime K <= kMaxTopk.
 // CH 16-byte vectors per lane per segment; segments are 64*CH vectors.
-template <int KT, int CH = kCombineSeg>
+template <int KT, int CH = kCombineSeg, int MODE = kCombinePairs>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
     if (wv >= a.num_tokens * a.segs)
         return;
-    const int t = wv / a.segs;
+    const int t = wv / a.segs;  // output row: a token, or a unit for kCombineUnitsIn
     const int sg = wv - t * a.segs;
     const int K = KT > 0 ? KT : a.topk;
+    if (a.row_count && t >= *a.row_count)
+        return;
 
-    int my_slot = -1;
-    float my_w = 0.0f;
-    if (lane < K) {
-        const int p = t * K + lane;
-        my_slot = a.slot_of[p];
-        if (my_slot >= 0)
-            my_w = a.weights ? a.weights[(size_t)my_slot * K + lane] : 1.0f;
-        if (a.out_weights && sg == 0)
-            a.out_weights[p] = my_w;
-    }
+    int my_slot;
+    float my_w;
+    combine_terms<MODE>(a, t, sg, lane, K, my_slot, my_w);
     // the token's first slot: a safe row to load for pairs that have none
     const uint64_t have = __ballot(my_slot >= 0);
     const int V = a.row_vecs;

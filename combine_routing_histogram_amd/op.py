@@ -75,6 +75,10 @@ class EpDispatchCombineOp:
         self._side_stream = None
         self._sent_dispatch = None
         self._sent_combine = None
+        self.u_cap = config.max_tokens * min(config.topk, config.num_ranks)
+        self._last_dedup = False
+        self._units = None          # unit-row buffers, allocated on first use
+        self._unit_carried = (False, False)
 
     def __del__(self):
         op = getattr(self, "_op", None)
@@ -155,6 +159,7 @@ class EpDispatchCombineOp:
         B.epdc_dispatch(self._op, self._stream(), T, i, w, s, _ptr(indices), o, ow, os_,
                         _ptr(self._out_indices), _ptr(self._recv_count))
         self._tokens = T
+        self._last_dedup = False
         return self._dispatch_views(weights, scales)
 
     def dispatch_replay(self, input: torch.Tensor, weights: Optional[torch.Tensor] = None,
@@ -163,14 +168,25 @@ class EpDispatchCombineOp:
         last dispatch (no histogram, scan or ranking).  Returns the views of
         dispatch(); indices and recv_count keep the recorded dispatch's values."""
         T = self._tokens
+        units = self._last_dedup
+        views = (lambda: self._unit_views(weights is not None, scales is not None)) if units \
+            else (lambda: self._dispatch_views(weights, scales))
         if T == 0:
             # nothing to move; the library still refuses a replay with no dispatch recorded
             B.epdc_dispatch_replay(self._op, self._stream(), 0, 0, 0, 0, 0, 0)
-            return self._dispatch_views(weights, scales)
+            return views()
         self._check_payload(input, weights, scales, T)
-        i, w, s, o, ow, os_ = self._dispatch_ptrs(input, weights, scales)
+        if units:  # a rank-deduplicated dispatch replays into the unit rows
+            ub = self._unit_buffers()
+            quant = self.config.quant != "none"
+            i, w, s = _ptr(input), _ptr(weights), _ptr(scales)
+            o = _ptr(ub["out"])
+            ow = _ptr(ub["weights"]) if weights is not None else 0
+            os_ = _ptr(ub["scales"]) if (scales is not None or quant) else 0
+        else:
+            i, w, s, o, ow, os_ = self._dispatch_ptrs(input, weights, scales)
         B.epdc_dispatch_replay(self._op, self._stream(), i, w, s, o, ow, os_)
-        return self._dispatch_views(weights, scales)
+        return views()
 
     def dispatch_send(self, input: torch.Tensor, weights: Optional[torch.Tensor],
                       scales: Optional[torch.Tensor], indices: torch.Tensor) -> None:
@@ -189,6 +205,7 @@ class EpDispatchCombineOp:
         B.epdc_dispatch_send(self._op, side.cuda_stream, T, i, w, s, _ptr(indices), o, ow, os_,
                              _ptr(self._out_indices), _ptr(self._recv_count))
         self._tokens = T
+        self._last_dedup = False
         self._sent_dispatch = (weights is not None, scales is not None)
 
     def dispatch_recv(self):
@@ -202,26 +219,31 @@ class EpDispatchCombineOp:
         return (self.received_payload(), self._out_weights if has_w else None,
                 self.received_scales(has_s), self._out_indices, self._recv_count)
 
-    def received_payload(self) -> torch.Tensor:
+    def _payload_view(self, buf: torch.Tensor) -> torch.Tensor:
         cfg = self.config
         if cfg.raw_row_bytes:
-            return self._out
+            return buf
         if cfg.quant == "none":
-            return self._out.view(torch.bfloat16)
+            return buf.view(torch.bfloat16)
         if cfg.quant == "fp8_e4m3_b128":
-            return self._out.view(torch.float8_e4m3fn)
-        return self._out
+            return buf.view(torch.float8_e4m3fn)
+        return buf
 
-    def received_scales(self, carried: bool = True) -> Optional[torch.Tensor]:
+    def _scales_view(self, buf: Optional[torch.Tensor], carried: bool) -> Optional[torch.Tensor]:
         cfg = self.config
         if cfg.quant == "fp8_e4m3_b128":
-            return self._out_scales.view(torch.float32)
+            return buf.view(torch.float32)
         if cfg.quant == "mxfp4_b32":
-            return self._out_scales
-        if not carried or self._out_scales is None:
+            return buf
+        if not carried or buf is None:
             return None
-        dt = self._scales_dtype or torch.uint8
-        return self._out_scales.view(dt)
+        return buf.view(self._scales_dtype or torch.uint8)
+
+    def received_payload(self) -> torch.Tensor:
+        return self._payload_view(self._out)
+
+    def received_scales(self, carried: bool = True) -> Optional[torch.Tensor]:
+        return self._scales_view(self._out_scales, carried)
 
     def combine(self, input: torch.Tensor, weights: Optional[torch.Tensor] = None,
                 indices: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -273,9 +295,120 @@ class EpDispatchCombineOp:
             if weights.dim() != 2 or weights.shape[0] < rows or weights.shape[1] != cfg.topk:
                 raise ValueError(f"combine weights must be [>= {rows}, topk] fp32")
 
+    # ---- rank-deduplicated dispatch and the standard-MoE conversion -------------------
+    def _unit_buffers(self) -> dict:
+        if self._units is None:
+            cfg, dev = self.config, self.device
+            u = self.u_cap
+            with torch.cuda.device(dev):
+                self._units = {
+                    "out": torch.empty((u, self.payload_row_bytes), dtype=torch.uint8, device=dev),
+                    "weights": torch.empty((u, cfg.topk), dtype=torch.float32, device=dev),
+                    "indices": torch.empty((u, cfg.topk), dtype=torch.int32, device=dev),
+                    "scales": (torch.empty((u, self.scale_row_bytes), dtype=torch.uint8,
+                                           device=dev) if self.scale_row_bytes else None),
+                    "recv": torch.empty(cfg.num_ranks, dtype=torch.int32, device=dev),
+                    "partial": torch.empty((u, cfg.hidden), dtype=torch.bfloat16, device=dev),
+                }
+        return self._units
+
+    def _unit_views(self, has_w: bool, has_s: bool):
+        ub = self._unit_buffers()
+        return (self._payload_view(ub["out"]), ub["weights"] if has_w else None,
+                self._scales_view(ub["scales"], has_s), ub["indices"], ub["recv"])
+
+    def dispatch_dedup(self, input: torch.Tensor, weights: Optional[torch.Tensor],
+                       scales: Optional[torch.Tensor], indices: torch.Tensor):
+        """Dispatch with one received row per (token, destination rank).
+
+        Returns (output, weights, scales, indices, recv_count) like dispatch()
+        but over unit rows: views of [U_cap, ...] buffers, U_cap = max_tokens *
+        min(topk, num_ranks); rank r owns rows [unit_off[r], unit_off[r+1])
+        (get_unit_routing) and recv_count[r] of them."""
+        T = int(indices.shape[0])
+        self._need(indices, "indices", torch.int32, (T, self.config.topk))
+        self._check_payload(input, weights, scales, T)
+        ub = self._unit_buffers()
+        quant = self.config.quant != "none"
+        B.epdc_dispatch_dedup(self._op, self._stream(), T, _ptr(input), _ptr(weights),
+                              _ptr(scales), _ptr(indices), _ptr(ub["out"]),
+                              _ptr(ub["weights"]) if weights is not None else 0,
+                              _ptr(ub["scales"]) if (scales is not None or quant) else 0,
+                              _ptr(ub["indices"]), _ptr(ub["recv"]))
+        self._tokens = T
+        self._last_dedup = True
+        self._unit_carried = (weights is not None, scales is not None)
+        return self._unit_views(*self._unit_carried)
+
+    def get_unit_routing(self):
+        """(unit_off [R+1], unit_of [T*K], unit_src [U_cap]) of the last
+        rank-deduplicated dispatch (only the first unit_off[R] of unit_src
+        are meaningful)."""
+        a, b, c = B.epdc_get_unit_routing(self._op)
+        cfg = self.config
+        return (self._ws_view(a, cfg.num_ranks + 1), self._ws_view(b, self._tokens * cfg.topk),
+                self._ws_view(c, self.u_cap))
+
+    def units_to_experts(self, input: Optional[torch.Tensor] = None,
+                         weights: Optional[torch.Tensor] = None,
+                         scales: Optional[torch.Tensor] = None,
+                         indices: Optional[torch.Tensor] = None):
+        """Standard-MoE conversion: expand unit rows (by default the op's own,
+        with whatever the last dispatch_dedup carried) into the expert-layout
+        rows dispatch() would have written; returns dispatch()'s views."""
+        if input is None:
+            has_w, has_s = self._unit_carried
+            ub = self._unit_buffers()
+            input, indices = ub["out"], ub["indices"]
+            weights = ub["weights"] if has_w else None
+            scales = ub["scales"] if (has_s or self.config.quant != "none") else None
+        for t, n in ((input, "input"), (weights, "weights"), (scales, "scales"),
+                     (indices, "indices")):
+            if t is not None:
+                self._need(t, n)
+        B.epdc_units_to_experts(self._op, self._stream(), _ptr(input), _ptr(weights),
+                                _ptr(scales), _ptr(indices), _ptr(self._out),
+                                _ptr(self._out_weights) if weights is not None else 0,
+                                _ptr(self._out_scales) if scales is not None else 0,
+                                _ptr(self._out_indices) if indices is not None else 0)
+        return (self.received_payload(), self._out_weights if weights is not None else None,
+                self.received_scales(scales is not None), self._out_indices, None)
+
+    def experts_to_units(self, input: torch.Tensor,
+                         weights: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Weighted sum of each unit's expert rows (bf16 [>= T*K, H] in the
+        expert layout, fp32 weights [>= T*K, K] or None) into bf16 unit rows
+        [U_cap, H] (an op-owned buffer)."""
+        self._check_combine(input, weights)
+        part = self._unit_buffers()["partial"]
+        B.epdc_experts_to_units(self._op, self._stream(), _ptr(input), _ptr(weights), _ptr(part))
+        return part
+
+    def combine_units(self, input: Optional[torch.Tensor] = None,
+                      weights: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+        """Sum each token's unit rows (by default the last experts_to_units
+        result); weights: the unit rows' fp32 [U_cap, K] weights to hand back
+        per token, or None.  Returns (output bf16 [T, H], weights fp32 [T, K])."""
+        cfg = self.config
+        ub = self._unit_buffers()
+        if input is None:
+            input = ub["partial"]
+        self._need(input, "input", torch.bfloat16)
+        if input.dim() != 2 or input.shape[1] != cfg.hidden or input.shape[0] < self.u_cap:
+            raise ValueError(f"unit rows must be bf16 [>= {self.u_cap}, {cfg.hidden}]")
+        if weights is not None:
+            self._need(weights, "weights", torch.float32)
+            if weights.dim() != 2 or weights.shape[0] < self.u_cap or weights.shape[1] != cfg.topk:
+                raise ValueError(f"unit weights must be fp32 [>= {self.u_cap}, {cfg.topk}]")
+        B.epdc_combine_units(self._op, self._stream(), _ptr(input), _ptr(weights),
+                             _ptr(self._combined), _ptr(self._combined_weights))
+        T = self._tokens
+        return self._combined[:T], self._combined_weights[:T]
+
     def reset(self) -> None:
         B.epdc_reset(self._op)
         self._tokens = 0
+        self._last_dedup = False
         self._sent_dispatch = self._sent_combine = None
 
     def get_dispatch_src_token_pos(self) -> torch.Tensor:

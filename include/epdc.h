@@ -112,7 +112,10 @@ enum {
     EPDC_KERNEL_SCATTER_FP8 = 3,   /* slot + E4M3 quantize + copy */
     EPDC_KERNEL_SCATTER_MXFP4 = 4, /* slot + MXFP4 quantize + copy */
     EPDC_KERNEL_COMBINE = 5,       /* gather + weighted fp32 sum */
-    EPDC_NUM_KERNELS = 6
+    EPDC_KERNEL_UNITS_TO_EXPERTS = 6, /* unit rows -> expert rows (conversion) */
+    EPDC_KERNEL_EXPERTS_TO_UNITS = 7, /* weighted sum of a unit's expert rows */
+    EPDC_KERNEL_COMBINE_UNITS = 8,    /* sum of a token's unit rows */
+    EPDC_NUM_KERNELS = 9
 };
 
 /* Bytes of device workspace an op with this config needs (host only, no GPU
@@ -184,13 +187,87 @@ epdc_status epdc_combine(epdc_op *op, void *stream, const void *input,
                          void *output, float *out_weights);
 
 /*
+ * Rank-deduplicated dispatch and the standard-MoE conversion.
+ *
+ * The pages name a standard-MoE conversion for the intra-node path ("Choosing
+ * an EP API and backend" page, "EP paths" table) and an intra-node kernel
+ * type ("Communication APIs" page, kernel types table) without defining
+ * them.  Reading implemented here: a token travels once to each destination
+ * rank that hosts at least one of its valid experts ("unit" (t, r)); the
+ * receiving rank expands its unit rows into the expert-contiguous rows of
+ * epdc_dispatch (epdc_units_to_experts) for the grouped expert GEMM; on the
+ * way back it sums the weighted outputs of each unit's experts into one bf16
+ * unit row (epdc_experts_to_units), and the source adds its token's unit
+ * rows (epdc_combine_units).  On several GPUs only unit rows would cross the
+ * links, min(K, R) per token at most instead of K.
+ *
+ * Unit rows: U = sum(recv_count) <= T * min(K, R); rank r owns rows
+ * [unit_off[r], unit_off[r+1]), ordered by token.  Unit row buffers need
+ * capacity U_cap = max_tokens * min(topk, num_ranks) rows.
+ */
+
+/* Like epdc_dispatch, with one received row per unit: out, out_weights,
+ * out_scales and out_indices are [U_cap, ...] in the unit layout (each unit
+ * carries its token's full weights / indices / scales rows), recv_count[r]
+ * = unit rows of rank r.  The pair routing (expert offsets, slot of each
+ * pair, source positions) is recorded as well, so epdc_combine,
+ * epdc_get_routing and epdc_get_dispatch_src_token_pos work after it as after
+ * epdc_dispatch, and epdc_dispatch_replay replays the unit rows. */
+epdc_status epdc_dispatch_dedup(epdc_op *op, void *stream, int32_t num_tokens,
+                                const void *input, const float *weights,
+                                const void *scales, const int32_t *indices,
+                                void *out, float *out_weights, void *out_scales,
+                                int32_t *out_indices, int32_t *recv_count);
+
+/* Device pointers of the last rank-deduplicated dispatch's unit routing:
+ * unit_off [R+1], unit_of [T*K] (unit row of each pair, -1 for an invalid
+ * expert id), unit_src [U] (token of each unit row).  Any output may be
+ * NULL.  BAD_STATE if the last dispatch was not rank-deduplicated. */
+epdc_status epdc_get_unit_routing(epdc_op *op, const int32_t **unit_off,
+                                  const int32_t **unit_of, const int32_t **unit_src);
+
+/* Conversion to the standard MoE layout: every unit row (payload bytes of
+ * the config, and the carried weights / scales / indices rows where given) is
+ * copied to the expert rows of its pairs, giving exactly the rows
+ * epdc_dispatch writes for the same input.  input [U_cap, P] (P = payload
+ * bytes per row as epdc_row_bytes reports), out [N_cap, P]; each carried
+ * array needs its input and output, or neither; scale rows must be a
+ * multiple of 4 bytes.  Reads the unit count on the device (no host wait).
+ * BAD_STATE if the last dispatch was not rank-deduplicated. */
+epdc_status epdc_units_to_experts(epdc_op *op, void *stream, const void *input,
+                                  const float *in_weights, const void *in_scales,
+                                  const int32_t *in_indices, void *out,
+                                  float *out_weights, void *out_scales,
+                                  int32_t *out_indices);
+
+/* Conversion back: unit row u of token t = bf16_rne(sum over k = 0..K-1 of
+ * the pairs of t in u of w(t,k) * in[slot(t,k)]) in fp32, separate multiply
+ * and add, w(t,k) = weights[slot(t,k)][k] (1 when weights is NULL).  input
+ * [N_cap, H] bf16 expert rows, weights [N_cap, K] fp32 or NULL, output
+ * [U_cap, H] bf16.  BAD_STATE if the last dispatch was not rank-deduplicated. */
+epdc_status epdc_experts_to_units(epdc_op *op, void *stream, const void *input,
+                                  const float *weights, void *output);
+
+/* Combine of unit rows: output[t] = bf16_rne(sum of the token's unit rows in
+ * ascending row order, i.e. ascending rank) in fp32 from +0 (+0 for a token
+ * with no valid pair); out_weights[t][k] = unit_weights[unit of (t,k)][k] (1
+ * when unit_weights is NULL, 0 for an invalid pair) or NULL.  input
+ * [U_cap, H] bf16, unit_weights [U_cap, K] fp32 or NULL, output [T, H].  It
+ * differs from epdc_combine on the same expert rows only by the bf16
+ * rounding of each unit's partial sum.  BAD_STATE as above. */
+epdc_status epdc_combine_units(epdc_op *op, void *stream, const void *input,
+                               const float *unit_weights, void *output,
+                               float *out_weights);
+
+/*
  * Routing replay: dispatch a new payload with the routing recorded by the last
  * dispatch (same tokens, same expert ids), skipping the histogram, scan and
  * ranking ("Choosing an EP API and backend" page, "EP paths" table: routing
  * replay).  Writes the payload, carried weights and scales rows to the same
  * slots; out_indices, recv_count, the offsets and src_token_pos are those of
  * the recorded dispatch and are not rewritten.  Arguments as in
- * epdc_dispatch, for num_tokens = the recorded dispatch's.  BAD_STATE if no
+ * epdc_dispatch, for num_tokens = the recorded dispatch's; after
+ * epdc_dispatch_dedup the rows written are unit rows.  BAD_STATE if no
  * dispatch is recorded.
  */
 epdc_status epdc_dispatch_replay(epdc_op *op, void *stream, const void *input,
