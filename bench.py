@@ -32,6 +32,39 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published figure
 
 
+def alg_bytes_units(kernel: str, w, units: int) -> int:
+    """Algorithmic bytes of the rank-deduplicated path's launches, for U =
+    `units` unit rows (one per (token, destination rank)):
+      dispatch scatter:   read x (2H) + weights and indices (8K) per token;
+                          write U rows (P + Q + 8K carried), slot_of,
+                          src_token_pos and unit_of (12K) per token, unit_src (4U)
+      units_to_experts:   read U rows (P + Q + 8K) and unit_src; read unit_of
+                          and slot_of (8K per token); write N rows (P + Q + 8K)
+      experts_to_units:   read N rows (2H) + one weight each (4N), the pair
+                          arrays (8N) and unit_src (4U); write U rows (2H)
+      combine_units:      read U rows (2H) + unit_of (4K per token); write T
+                          rows (2H) and their K weights read back (8K)
+    """
+    T, H, K = w.tokens, w.hidden, w.topk
+    N = T * K
+    U = units
+    P, Q = {"none": (2 * H, 0), "fp8_e4m3_b128": (H, 4 * H // 128),
+            "mxfp4_b32": (H // 2, H // 32)}[w.quant]
+    if kernel.startswith("k_scatter"):
+        return T * (2 * H + 8 * K + 12 * K) + U * (P + Q + 8 * K + 4)
+    if kernel == "k_units_to_experts":
+        return U * (P + Q + 8 * K + 4) + 8 * N + N * (P + Q + 8 * K)
+    if kernel == "k_experts_to_units":
+        return N * (2 * H + 4 + 8) + U * (4 + 2 * H)
+    if kernel == "k_combine_units":
+        return U * 2 * H + T * (4 * K + 2 * H + 8 * K)
+    if kernel == "k_route_rank":
+        return 8 * N * 2
+    if kernel == "k_route_scan":
+        return 0
+    raise ValueError(kernel)
+
+
 def alg_bytes(kernel: str, w) -> int:
     """Algorithmic bytes one launch of `kernel` must move for workload w.
 
@@ -77,7 +110,8 @@ def load_traffic(kernel: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, inp, budget_s: float, gpu_payload, gpu_scales, gpu_combined):
+def cpu_baseline(w, inp, budget_s: float, gpu_payload, gpu_scales, gpu_combined,
+                 dedup: bool = False):
     """Time the oracle (plain C, one thread) on whole steps of the workload,
     and compare its last step with the GPU's last timed step (payload bytes,
     produced scales, combine output)."""
@@ -88,21 +122,33 @@ def cpu_baseline(w, inp, budget_s: float, gpu_payload, gpu_scales, gpu_combined)
     identity = w.combine_input == "identity"
     reps, t0 = 0, time.perf_counter()
     while True:
-        d = oracle.dispatch(inp["x"], inp["weights"], inp["indices"], w.experts, w.ranks,
-                            quant=w.quant)
-        c_in = d["out"] if identity else inp["combine_input"]
-        y, _ = oracle.combine(c_in, d["out_weights"], d["slot_of"], w.tokens, w.topk)
+        if not dedup:
+            d = oracle.dispatch(inp["x"], inp["weights"], inp["indices"], w.experts, w.ranks,
+                                quant=w.quant)
+            c_in = d["out"] if identity else inp["combine_input"]
+            y, _ = oracle.combine(c_in, d["out_weights"], d["slot_of"], w.tokens, w.topk)
+        else:
+            d = oracle.dispatch_dedup(inp["x"], inp["weights"], inp["indices"], w.experts,
+                                      w.ranks, quant=w.quant)
+            n = d["n_valid"]
+            e_out = oracle.units_to_experts(d["out"], d["slot_of"], d["unit_of"], n)
+            e_w = oracle.units_to_experts(d["out_weights"], d["slot_of"], d["unit_of"], n)
+            c_in = e_out if identity else inp["combine_input"]
+            part = oracle.experts_to_units(c_in, e_w, d["unit_src"], d["unit_of"], d["slot_of"],
+                                           w.topk)
+            y, _ = oracle.combine_units(part, d["out_weights"], d["unit_of"], w.tokens, w.topk)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 50:
             break
-    n = d["n_valid"]
+    n = d["units"] if dedup else d["n_valid"]
     same = (np.array_equal(gpu_payload[:n], d["out"].view(np.uint8).reshape(n, -1))
             and np.array_equal(gpu_combined, y))
     if d["out_scales"] is not None:
         same = same and np.array_equal(gpu_scales[:n], d["out_scales"].view(np.uint8).reshape(n, -1))
     base = {"value": w.tokens * reps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} whole dispatch+combine steps of {w.name} "
+            "sample": f"{reps} whole {'rank-deduplicated ' if dedup else ''}"
+                      f"dispatch+combine steps of {w.name} "
                       f"({w.tokens} tokens each), {el:.1f} s"}
     return base, ("bit-exact" if same else "MISMATCH")
 
@@ -113,6 +159,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="deepseek_v3_bf16")
+    ap.add_argument("--path", choices=["pair", "dedup"], default="pair",
+                    help="pair: dispatch / combine with one row per (token, k) (default); "
+                         "dedup: rank-deduplicated dispatch, conversion to the expert layout, "
+                         "conversion back and unit combine")
     ap.add_argument("--kernel-events", choices=["timed", "separate"], default="separate",
                     help="record the per-kernel events in the timed steps, or (default) in a "
                          "second pass of the same number of steps right after them: each "
@@ -161,9 +211,16 @@ def main() -> int:
     op = EpDispatchCombineOp(EpDispatchCombineConfig(w.tokens, w.hidden, w.topk, w.experts,
                                                      w.ranks, quant=w.quant), dev)
 
+    dedup = args.path == "dedup"
+
     def step():
-        out, out_w, _, out_idx, _ = op.dispatch(x, wts, None, idx)
-        return op.combine(out if identity else c_in, out_w, out_idx)
+        if not dedup:
+            out, out_w, _, out_idx, _ = op.dispatch(x, wts, None, idx)
+            return op.combine(out if identity else c_in, out_w, out_idx)
+        _, u_w, _, _, _ = op.dispatch_dedup(x, wts, None, idx)
+        e_out, e_w, _, _, _ = op.units_to_experts()
+        op.experts_to_units(e_out if identity else c_in, e_w)
+        return op.combine_units(None, u_w)
 
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib << 20
@@ -176,6 +233,7 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    units = int(op.get_unit_routing()[0][-1]) if dedup else None
     timed_step = step
     if args.graph:
         side = torch.cuda.Stream()
@@ -201,7 +259,7 @@ def main() -> int:
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     timed_events = args.kernel_events == "timed" and not args.graph
     if timed_events:
-        op.profile_begin(4 * args.steps)
+        op.profile_begin(8 * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
@@ -211,7 +269,7 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     if not timed_events:
-        op.profile_begin(4 * args.steps)
+        op.profile_begin(8 * args.steps)
         for _ in range(args.steps):
             step()
         torch.cuda.synchronize()
@@ -226,7 +284,7 @@ def main() -> int:
     cold = None
     if args.cold_steps > 0:
         scratch = torch.empty(256 << 20, dtype=torch.int16, device=dev)
-        op.profile_begin(4 * args.cold_steps)
+        op.profile_begin(8 * args.cold_steps)
         for i in range(args.cold_steps):
             scratch.fill_(i)          # writes 512 MiB with a fill kernel
             step()
@@ -236,9 +294,12 @@ def main() -> int:
     ms_step = wall * 1e3 / args.steps
     tokens_per_s = w.tokens / (ms_step * 1e-3)
 
+    def kbytes(name):
+        return alg_bytes_units(name, w, units) if dedup else alg_bytes(name, w)
+
     kernels = {}
     for name, (ms, n) in prof.items():
-        b = alg_bytes(name, w)
+        b = kbytes(name)
         avg = ms / n
         kernels[name] = {"launches": n, "avg_us": avg * 1e3, "alg_bytes": b,
                          "gbps": b / (avg * 1e-3) / 1e9 if b else None,
@@ -247,7 +308,7 @@ def main() -> int:
     if cold is not None:
         cold_kernels = {}
         for name, (ms, n) in cold.items():
-            b = alg_bytes(name, w)
+            b = kbytes(name)
             avg = ms / n
             cold_kernels[name] = {"avg_us": avg * 1e3,
                                   "frac": b / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS if b else None}
@@ -258,13 +319,18 @@ def main() -> int:
     # are workspace traffic, not counted)
     scatter_name = {"none": "k_scatter_copy", "fp8_e4m3_b128": "k_scatter_fp8",
                     "mxfp4_b32": "k_scatter_mxfp4"}[w.quant]
-    step_bytes = alg_bytes(scatter_name, w) + alg_bytes("k_combine", w)
-    traffic = load_traffic(dom, w.name)
+    if dedup:
+        step_bytes = sum(kbytes(k) for k in (scatter_name, "k_units_to_experts",
+                                              "k_experts_to_units", "k_combine_units"))
+    else:
+        step_bytes = alg_bytes(scatter_name, w) + alg_bytes("k_combine", w)
+    traffic = None if dedup else load_traffic(dom, w.name)
 
     result = {
-        "metric": "dispatch+combine tokens/s and achieved HBM GB/s (% peak), 4096x7168 top-8"
-                  if w.name == "deepseek_v3_bf16" else
-                  f"dispatch+combine tokens/s and achieved HBM GB/s (% peak), {w.name}",
+        "metric": ("dispatch+combine tokens/s and achieved HBM GB/s (% peak), 4096x7168 top-8"
+                   if w.name == "deepseek_v3_bf16" else
+                   f"dispatch+combine tokens/s and achieved HBM GB/s (% peak), {w.name}")
+                  + (" [rank-deduplicated dispatch + standard-MoE conversion]" if dedup else ""),
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -283,6 +349,8 @@ def main() -> int:
                    "combine_input": "identity (dispatch output)" if identity
                    else "independent N(0,1) bf16 rows",
                    "graph_mode": "hip graph replay" if args.graph else "eager",
+                   "path": args.path,
+                   "unit_rows": units,
                    "gpu": torch.cuda.get_device_name(dev)},
         "step_alg_bytes": step_bytes,
         "step_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
@@ -300,12 +368,17 @@ def main() -> int:
     parity = "skipped"
     result["cpu_baseline"] = None
     if args.cpu_seconds > 0:
-        payload = op.received_payload().view(torch.uint8).cpu().numpy()
-        scales = op.received_scales(False)
-        scales = None if scales is None else scales.view(torch.uint8).cpu().numpy()
+        if dedup:
+            payload = op.received_unit_payload().view(torch.uint8).cpu().numpy()
+            scales = op.received_unit_scales(False)
+            scales = None if scales is None else scales.view(torch.uint8).cpu().numpy()
+        else:
+            payload = op.received_payload().view(torch.uint8).cpu().numpy()
+            scales = op.received_scales(False)
+            scales = None if scales is None else scales.view(torch.uint8).cpu().numpy()
         combined = y.view(torch.int16).cpu().numpy().view(np.uint16)
         result["cpu_baseline"], parity = cpu_baseline(w, inp, args.cpu_seconds, payload, scales,
-                                                      combined)
+                                                      combined, dedup)
     result["parity"] = parity
     print(json.dumps(result), flush=True)
     return 0 if parity != "MISMATCH" else 1

@@ -1013,6 +1013,58 @@ __device__ inline void accumulate_row(float *acc, float w, u32x4 x)
     acc[7] = acc[7] + w * bf16_hi(x.w);
 }
 
+// CH vectors per lane of row s's segment starting at vector `base`.
+template <int CH>
+__device__ inline void load_segment(const u32x4 *in, int s, int V, int base, int lane,
+                                    u32x4 *dst)
+{
+    const u32x4 *row = in + (size_t)s * V;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int j = base + lane + kWave * i;
+        dst[i] = j < V ? __builtin_nontemporal_load(row + j) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// Sum of NT rows, lane k < NT holding the k-th slot and weight: the segment
+// of row k+1 loads while row k is accumulated.  NT is a compile-time count so
+// no load sits behind a branch and the wait counters stay exact.
+template <int NT, int CH>
+__device__ inline void sum_rows(const u32x4 *in, int V, int base, int lane, int my_slot,
+                                float my_w, float (&acc)[CH][8])
+{
+    int slot[NT];
+    float w[NT];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+        slot[k] = read_lane(my_slot, k);
+        w[k] = read_lane_f(my_w, k);
+    }
+    u32x4 buf[2][CH];
+    load_segment<CH>(in, slot[0], V, base, lane, buf[0]);
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+        if (k + 1 < NT)
+            load_segment<CH>(in, slot[k + 1], V, base, lane, buf[(k + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+            accumulate_row(acc[i], w[k], buf[k & 1][i]);
+    }
+}
+
+// sum_rows for the wave-uniform count n in [1, KT] (nothing for n == 0).
+template <int KT, int CH, int NT = 1>
+__device__ inline void sum_rows_n(int n, const u32x4 *in, int V, int base, int lane, int my_slot,
+                                  float my_w, float (&acc)[CH][8])
+{
+    if constexpr (NT <= KT) {
+        if (n == NT)
+            sum_rows<NT, CH>(in, V, base, lane, my_slot, my_w, acc);
+        else
+            sum_rows_n<KT, CH, NT + 1>(n, in, V, base, lane, my_slot, my_w, acc);
+    }
+}
+
 // KT = K known at compile time (double-buffered), or 0: runtime K <= kMaxTopk.
 // CH 16-byte vectors per lane per segment; segments are 64*CH vectors.
 template <int KT, int CH = kCombineSeg, int MODE = kCombinePairs>
@@ -1031,22 +1083,28 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
     int my_slot;
     float my_w;
     combine_terms<MODE>(a, t, sg, lane, K, my_slot, my_w);
-    // the token's first slot: a safe row to load for pairs that have none
+    // the terms with a row move to the front lanes, in lane order (the
+    // summation order is unchanged: terms without a row add nothing)
     const uint64_t have = __ballot(my_slot >= 0);
+    const int n = __popcll(have);
+    if constexpr (MODE != kCombineUnitsOut) {  // units-out terms are already compact
+        const int r = my_slot >= 0 ? lanes_below(have) : kWave;
+        int cs = -1;
+        float cw = 0.0f;
+        for (int j = 0; j < K; ++j) {
+            const int sj = __shfl(my_slot, j, kWave);
+            const float wj = __shfl(my_w, j, kWave);
+            if (__shfl(r, j, kWave) == lane) {
+                cs = sj;
+                cw = wj;
+            }
+        }
+        my_slot = cs;
+        my_w = cw;
+    }
     const int V = a.row_vecs;
     const int base = sg * kWave * CH;
     u32x4 *out = reinterpret_cast<u32x4 *>(a.output) + (size_t)t * V;
-    if (have == 0) {  // no pair of this token has a row: the sum is +0
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int j = base + lane + kWave * i;
-            if (j < V)
-                __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, out + j);
-        }
-        return;
-    }
-    const int fallback = read_lane(my_slot, __builtin_ctzll(have));
-
     const u32x4 *in = reinterpret_cast<const u32x4 *>(a.input);
     float acc[CH][8];
 #pragma unroll
@@ -1055,43 +1113,14 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
         for (int q = 0; q < 8; ++q)
             acc[i][q] = 0.0f;
 
-    auto load_row = [&](int s, u32x4 *dst) {
-        const u32x4 *row = in + (size_t)s * V;
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int j = base + lane + kWave * i;
-            dst[i] = j < V ? __builtin_nontemporal_load(row + j) : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-
     if constexpr (KT > 0) {
-        int slot[KT];
-        float w[KT];
-#pragma unroll
-        for (int k = 0; k < KT; ++k) {
-            slot[k] = read_lane(my_slot, k);
-            w[k] = read_lane_f(my_w, k);
-        }
-        u32x4 buf[2][CH];
-        load_row(slot[0] >= 0 ? slot[0] : fallback, buf[0]);
-#pragma unroll
-        for (int k = 0; k < KT; ++k) {
-            if (k + 1 < KT)
-                load_row(slot[k + 1] >= 0 ? slot[k + 1] : fallback, buf[(k + 1) & 1]);
-            if (slot[k] >= 0) {
-#pragma unroll
-                for (int i = 0; i < CH; ++i)
-                    accumulate_row(acc[i], w[k], buf[k & 1][i]);
-            }
-        }
+        // n == 0 leaves the sum at +0
+        sum_rows_n<KT, CH>(n, in, V, base, lane, my_slot, my_w, acc);
     } else {
-        for (int k = 0; k < K; ++k) {
-            const int s = read_lane(my_slot, k);
-            if (s < 0)
-                continue;
-            const float wk = read_lane_f(my_w, k);
+        for (int k = 0; k < n; ++k) {
             u32x4 buf[CH];
-            load_row(s, buf);
+            load_segment<CH>(in, read_lane(my_slot, k), V, base, lane, buf);
+            const float wk = read_lane_f(my_w, k);
 #pragma unroll
             for (int i = 0; i < CH; ++i)
                 accumulate_row(acc[i], wk, buf[i]);

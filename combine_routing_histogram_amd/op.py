@@ -312,6 +312,13 @@ class EpDispatchCombineOp:
                 }
         return self._units
 
+    def received_unit_payload(self) -> torch.Tensor:
+        """The unit rows of the last rank-deduplicated dispatch ([U_cap, ...])."""
+        return self._payload_view(self._unit_buffers()["out"])
+
+    def received_unit_scales(self, carried: bool = True) -> Optional[torch.Tensor]:
+        return self._scales_view(self._unit_buffers()["scales"], carried)
+
     def _unit_views(self, has_w: bool, has_s: bool):
         ub = self._unit_buffers()
         return (self._payload_view(ub["out"]), ub["weights"] if has_w else None,
