@@ -316,6 +316,51 @@ void oracle_combine(int T, int H, int K, const int32_t *slot_of,
     free(w);
 }
 
+/* ---- scatter combine: experts push, the token side reduces -------------- */
+
+/*
+ * The pages list a scatter combine next to the gather combine ("Choosing an
+ * EP API and backend" page, "EP paths" table, FlyDSL row) without defining
+ * it.  Reading: the expert side pushes each received row, multiplied by its
+ * weight in fp32, to a staging row of the token it came from (one staging row
+ * per pair, so no two pushes meet), and the token side adds its K staging
+ * rows in k order.  Step 1: staging[src_token_pos[s]] = w(s) * f32(in[s]) for
+ * each received row s < n_rows, w(s) = weights[s][k] with k the pair's k (1
+ * when weights is NULL).  Step 2: out[t] = bf16_rne(sum over k = 0..K-1 with
+ * slot_of[t*K+k] >= 0 of staging[t*K+k]) from +0.0f; out_weights as in
+ * oracle_combine.
+ */
+void oracle_combine_push(int n_rows, int T, int H, int K, const int32_t *src_token_pos,
+                         const int32_t *slot_of, const uint16_t *in, const float *weights,
+                         float *staging, uint16_t *out, float *out_weights)
+{
+    for (int s = 0; s < n_rows; ++s) {
+        long p = src_token_pos[s];
+        int k = (int)(p % K);
+        float w = weights ? weights[(long)s * K + k] : 1.0f;
+        for (int h = 0; h < H; ++h)
+            staging[p * H + h] = w * bf16_to_f32(in[(long)s * H + h]);
+    }
+    for (int t = 0; t < T; ++t) {
+        for (int k = 0; k < K; ++k) {
+            int32_t s = slot_of[(long)t * K + k];
+            if (out_weights)
+                out_weights[(long)t * K + k] =
+                    s < 0 ? 0.0f : (weights ? weights[(long)s * K + k] : 1.0f);
+        }
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k) {
+                long p = (long)t * K + k;
+                if (slot_of[p] < 0)
+                    continue;
+                acc = acc + staging[p * H + h];
+            }
+            out[(long)t * H + h] = f32_to_bf16_rne(acc);
+        }
+    }
+}
+
 /* ---- rank-deduplicated dispatch and the standard-MoE conversion --------- */
 
 /*

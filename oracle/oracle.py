@@ -58,6 +58,7 @@ def _load():
     lib.oracle_quant_mxfp4.restype = I
     lib.oracle_combine.argtypes = [I, I, I, P, P, P, P, P]
     lib.oracle_combine.restype = None
+    lib.oracle_combine_push.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
     lib.oracle_route_units.argtypes = [I, I, I, I, P, P, P, P, P]
     lib.oracle_route_units.restype = I
     lib.oracle_gather_rows.argtypes = [I, P, P, L, P]
@@ -214,6 +215,26 @@ def combine(inp: np.ndarray, weights: Optional[np.ndarray], slot_of: np.ndarray,
     _load().oracle_combine(int(tokens), H, int(topk), _ptr(so), _ptr(x), _ptr(w),
                            _ptr(out), _ptr(out_w))
     return out, out_w
+
+
+# ---- scatter combine ------------------------------------------------------------
+
+def combine_push(inp: np.ndarray, weights: Optional[np.ndarray], src_token_pos: np.ndarray,
+                 slot_of: np.ndarray, tokens: int, topk: int):
+    """Scatter combine: each received row, weighted in fp32, pushed to its
+    pair's staging row; each token adds its staging rows in k order.
+    Returns (bf16 bits [T,H], fp32 [T,K], the fp32 staging rows [T*K,H])."""
+    x = _c(inp, np.uint16)
+    H = x.shape[1]
+    src = _c(src_token_pos, np.int32)
+    so = _c(slot_of, np.int32)
+    w = None if weights is None else _c(weights, np.float32)
+    staging = np.zeros((tokens * topk, H), np.float32)
+    out = np.empty((tokens, H), np.uint16)
+    out_w = np.empty((tokens, topk), np.float32)
+    _load().oracle_combine_push(src.size, int(tokens), H, int(topk), _ptr(src), _ptr(so), _ptr(x),
+                                _ptr(w), _ptr(staging), _ptr(out), _ptr(out_w))
+    return out, out_w, staging
 
 
 # ---- rank-deduplicated dispatch and the standard-MoE conversion ------------------

@@ -152,3 +152,32 @@ def test_dispatch_carries_rows():
     np.testing.assert_array_equal(d["out_weights"], inp["weights"][tok])
     np.testing.assert_array_equal(d["out_indices"], inp["indices"][tok])
     np.testing.assert_array_equal(d["out_scales"], sc[tok])
+
+
+def test_push_combine_is_the_gather_combine():
+    """Scatter combine (push weighted rows to per-pair staging rows, then add
+    them in k order) forms the same fp32 products and adds them in the same
+    order as the gather combine, so the two agree bit for bit; the staging
+    rows hold w * x exactly."""
+    rng = np.random.default_rng(31)
+    T, H, K, E, R = 150, 96, 6, 24, 4
+    idx = wl.draw_topk(rng, T, E, K, "zipf", 1.2)
+    idx[4, 1], idx[9, 5] = -1, E          # pairs without a row
+    x = wl.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    wts = wl.softmax_weights(rng, T, K)
+    d = oracle.dispatch(x, wts, idx, E, R)
+    c_in = wl.f32_to_bf16_bits(rng.standard_normal((d["n_valid"], H)).astype(np.float32))
+    for w in (d["out_weights"], None):
+        y1, yw1 = oracle.combine(c_in, w, d["slot_of"], T, K)
+        y2, yw2, st = oracle.combine_push(c_in, w, d["src_token_pos"], d["slot_of"], T, K)
+        np.testing.assert_array_equal(y2, y1)
+        np.testing.assert_array_equal(yw2.view(np.uint32), yw1.view(np.uint32))
+        # staging row of pair p = its weight times its received row, in fp32
+        xin = wl.bf16_bits_to_f32(c_in)
+        for p in (0, 7, 100, T * K - 1):
+            s = d["slot_of"][p]
+            if s < 0:
+                assert not st[p].any()
+                continue
+            wk = np.float32(1.0) if w is None else w[s, p % K]
+            np.testing.assert_array_equal(st[p], (wk * xin[s]).astype(np.float32))
