@@ -84,6 +84,14 @@ def alg_bytes(kernel: str, w) -> int:
         per = 2 * H + 8 * K + K * (P + Q) + 8 * K * K + 8 * K
     elif kernel == "k_combine":
         per = 2 * K * H + 8 * K + 2 * H + 4 * K
+    elif kernel == "k_combine_push":
+        # read each received row (2H) and its weight and pair (8); write the
+        # fp32 products to the pair's staging row (4H)
+        per = K * (2 * H + 8 + 4 * H)
+    elif kernel == "k_combine_reduce":
+        # read the K staging rows (4KH) + slot_of and weights (8K); write the
+        # row (2H) and its K weights (4K)
+        per = 4 * K * H + 8 * K + 2 * H + 4 * K
     elif kernel == "k_route_rank":
         per = 8 * K
     elif kernel == "k_route_scan":
@@ -163,6 +171,8 @@ def main() -> int:
                     help="pair: dispatch / combine with one row per (token, k) (default); "
                          "dedup: rank-deduplicated dispatch, conversion to the expert layout, "
                          "conversion back and unit combine")
+    ap.add_argument("--combine", choices=["gather", "scatter"], default="gather",
+                    help="pair path only: gather combine (default) or scatter (push) combine")
     ap.add_argument("--kernel-events", choices=["timed", "separate"], default="separate",
                     help="record the per-kernel events in the timed steps, or (default) in a "
                          "second pass of the same number of steps right after them: each "
@@ -216,7 +226,8 @@ def main() -> int:
     def step():
         if not dedup:
             out, out_w, _, out_idx, _ = op.dispatch(x, wts, None, idx)
-            return op.combine(out if identity else c_in, out_w, out_idx)
+            comb = op.combine_scatter if args.combine == "scatter" else op.combine
+            return comb(out if identity else c_in, out_w, out_idx)
         _, u_w, _, _, _ = op.dispatch_dedup(x, wts, None, idx)
         e_out, e_w, _, _, _ = op.units_to_experts()
         op.experts_to_units(e_out if identity else c_in, e_w)
@@ -322,6 +333,9 @@ def main() -> int:
     if dedup:
         step_bytes = sum(kbytes(k) for k in (scatter_name, "k_units_to_experts",
                                               "k_experts_to_units", "k_combine_units"))
+    elif args.combine == "scatter":
+        step_bytes = (alg_bytes(scatter_name, w) + alg_bytes("k_combine_push", w)
+                      + alg_bytes("k_combine_reduce", w))
     else:
         step_bytes = alg_bytes(scatter_name, w) + alg_bytes("k_combine", w)
     traffic = None if dedup else load_traffic(dom, w.name)
@@ -330,7 +344,8 @@ def main() -> int:
         "metric": ("dispatch+combine tokens/s and achieved HBM GB/s (% peak), 4096x7168 top-8"
                    if w.name == "deepseek_v3_bf16" else
                    f"dispatch+combine tokens/s and achieved HBM GB/s (% peak), {w.name}")
-                  + (" [rank-deduplicated dispatch + standard-MoE conversion]" if dedup else ""),
+                  + (" [rank-deduplicated dispatch + standard-MoE conversion]" if dedup else "")
+                  + (" [scatter combine]" if args.combine == "scatter" and not dedup else ""),
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -350,6 +365,7 @@ def main() -> int:
                    else "independent N(0,1) bf16 rows",
                    "graph_mode": "hip graph replay" if args.graph else "eager",
                    "path": args.path,
+                   "combine": args.combine,
                    "unit_rows": units,
                    "gpu": torch.cuda.get_device_name(dev)},
         "step_alg_bytes": step_bytes,

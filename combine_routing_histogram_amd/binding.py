@@ -40,7 +40,9 @@ EPDC_KERNEL_COMBINE = 5
 EPDC_KERNEL_UNITS_TO_EXPERTS = 6
 EPDC_KERNEL_EXPERTS_TO_UNITS = 7
 EPDC_KERNEL_COMBINE_UNITS = 8
-EPDC_NUM_KERNELS = 9
+EPDC_KERNEL_COMBINE_PUSH = 9
+EPDC_KERNEL_COMBINE_REDUCE = 10
+EPDC_NUM_KERNELS = 11
 
 
 class epdc_config(ctypes.Structure):
@@ -77,6 +79,7 @@ _SIGNATURES = {
     "epdc_combine_recv": (I32, [P, P]),
     "epdc_get_dispatch_src_token_pos": (I32, [P, ctypes.POINTER(P), PI32]),
     "epdc_get_routing": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P)]),
+    "epdc_combine_scatter": (I32, [P, P, P, P, P, P, P, P]),
     "epdc_dispatch_dedup": (I32, [P, P, I32, P, P, P, P, P, P, P, P, P]),
     "epdc_get_unit_routing": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P)]),
     "epdc_units_to_experts": (I32, [P, P, P, P, P, P, P, P, P, P]),
@@ -208,6 +211,13 @@ def epdc_get_routing(op: int) -> Tuple[int, int, int]:
     a, b, c = P(None), P(None), P(None)
     _check(lib().epdc_get_routing(op, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
     return a.value, b.value, c.value
+
+
+def epdc_combine_scatter(op: int, stream: int, input: int, weights: int, indices: int,
+                         staging: int, output: int, out_weights: int) -> None:
+    _check(lib().epdc_combine_scatter(op, stream or None, input or None, weights or None,
+                                      indices or None, staging or None, output or None,
+                                      out_weights or None))
 
 
 def epdc_dispatch_dedup(op: int, stream: int, num_tokens: int, input: int, weights: int,

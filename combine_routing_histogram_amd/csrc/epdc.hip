@@ -158,7 +158,8 @@ void row_bytes_for(const epdc_config &c, size_t *payload, size_t *scales)
 
 const char *const kKernelNames[EPDC_NUM_KERNELS] = {
     "k_route_rank", "k_route_scan", "k_scatter_copy", "k_scatter_fp8", "k_scatter_mxfp4",
-    "k_combine", "k_units_to_experts", "k_experts_to_units", "k_combine_units"};
+    "k_combine", "k_units_to_experts", "k_experts_to_units", "k_combine_units",
+    "k_combine_push", "k_combine_reduce"};
 
 }  // namespace
 
@@ -845,6 +846,63 @@ epdc_status epdc_combine(epdc_op *op, void *stream, const void *input, const flo
     (void)c;
     const epdc_status s = launch_combine_mode<kCombinePairs>(
         op, static_cast<hipStream_t>(stream), EPDC_KERNEL_COMBINE, ca, T);
+    return s == EPDC_SUCCESS ? ok() : s;
+}
+
+epdc_status epdc_combine_scatter(epdc_op *op, void *stream, const void *input,
+                                 const float *weights, const int32_t *indices, float *staging,
+                                 void *output, float *out_weights)
+{
+    (void)indices;  // the op keeps the routing of the last dispatch
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    if (!op->routed)
+        return fail(EPDC_ERR_BAD_STATE, "combine needs a dispatch first (none since create/reset)");
+    const epdc_config &c = op->cfg;
+    const int T = op->last_tokens;
+    if (T == 0)
+        return ok();
+    if (!input || !staging || !output)
+        return fail(EPDC_ERR_INVALID_ARGS, "input, staging and output are required");
+    if (!aligned(input, 16) || !aligned(staging, 16) || !aligned(output, 16) ||
+        !aligned(weights, 4) || !aligned(out_weights, 4))
+        return fail(EPDC_ERR_INVALID_ARGS,
+                    "input/staging/output must be 16-byte aligned, weights 4-byte aligned");
+    constexpr int CH = kCombineSeg;
+    PushArgs pa = {};
+    pa.rows = T * c.topk;
+    pa.row_count = op->i32(op->lay.expert_off) + c.num_experts;
+    pa.topk = c.topk;
+    pa.row_vecs = c.hidden / 8;
+    pa.segs = (pa.row_vecs + kWave * CH - 1) / (kWave * CH);
+    pa.n_pairs = T * c.topk;
+    pa.src_pos = op->i32(op->lay.src_pos);
+    pa.slot_of = op->i32(op->lay.slot_of);
+    pa.input = static_cast<const uint8_t *>(input);
+    pa.weights = weights;
+    pa.staging = staging;
+    pa.output = static_cast<uint8_t *>(output);
+    pa.out_weights = out_weights;
+    pa.num_tokens = T;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int grid, block;
+    epdc_status s = grid_for_waves((int64_t)pa.rows * pa.segs, &grid, &block);
+    if (s == EPDC_SUCCESS)
+        s = launch(op, st, EPDC_KERNEL_COMBINE_PUSH,
+                   [&] { k_combine_push<CH><<<grid, block, 0, st>>>(pa); });
+    if (s == EPDC_SUCCESS)
+        s = grid_for_waves((int64_t)T * pa.segs, &grid, &block);
+    if (s == EPDC_SUCCESS)
+        s = launch(op, st, EPDC_KERNEL_COMBINE_REDUCE, [&] {
+            switch (c.topk) {
+            case 1: k_combine_reduce<1, CH><<<grid, block, 0, st>>>(pa); break;
+            case 2: k_combine_reduce<2, CH><<<grid, block, 0, st>>>(pa); break;
+            case 4: k_combine_reduce<4, CH><<<grid, block, 0, st>>>(pa); break;
+            case 6: k_combine_reduce<6, CH><<<grid, block, 0, st>>>(pa); break;
+            case 8: k_combine_reduce<8, CH><<<grid, block, 0, st>>>(pa); break;
+            default: k_combine_reduce<0, CH><<<grid, block, 0, st>>>(pa); break;
+            }
+        });
     return s == EPDC_SUCCESS ? ok() : s;
 }
 

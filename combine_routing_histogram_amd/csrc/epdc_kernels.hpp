@@ -24,6 +24,7 @@ namespace epdc {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
@@ -1131,6 +1132,187 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
     // read-dominated kernel down by 10-13% when its input rows come from HBM
     // (measured on gfx950); they are 2-3% faster only when half the input is
     // still in the MALL from the scatter that just wrote it.
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int j = base + lane + kWave * i;
+        if (j < V)
+            __builtin_nontemporal_store(
+                u32x4{pack_bf16_rne(acc[i][0], acc[i][1]), pack_bf16_rne(acc[i][2], acc[i][3]),
+                      pack_bf16_rne(acc[i][4], acc[i][5]), pack_bf16_rne(acc[i][6], acc[i][7])},
+                out + j);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Scatter combine: the expert side pushes, the token side reduces
+// ---------------------------------------------------------------------------
+//
+// Push: one wave per (received row s, 2 KiB segment) multiplies the bf16 row
+// by its weight in fp32 and writes the products to the fp32 staging row of
+// the pair it came from (src_token_pos[s]); no two rows share a staging row,
+// so there are no atomics and no order to fix.  Reduce: one wave per
+// (token, segment) adds the token's staging rows in k order.  The products
+// and the order are the gather combine's, so the result is bit-identical to
+// it; the staging round trip costs 4 extra bytes per element each way, which
+// is what a one-sided push across GPUs would pay on the link instead.
+
+struct PushArgs {
+    int32_t rows;               // grid rows (received-row capacity of the call)
+    const int32_t *row_count;   // device count of received rows
+    int32_t topk;
+    int32_t row_vecs;           // 16-byte vectors per bf16 row (H/8)
+    int32_t segs;
+    int32_t n_pairs;
+    const int32_t *src_pos;     // [rows]: pair of each received row
+    const int32_t *slot_of;     // [T*K]
+    const uint8_t *input;       // [rows, H] bf16
+    const float *weights;       // [rows, K] or NULL
+    float *staging;             // [T*K, H] fp32
+    uint8_t *output;            // [T, H] bf16
+    float *out_weights;         // [T, K] or NULL
+    int32_t num_tokens;
+};
+
+template <int CH>
+__global__ __launch_bounds__(256) void k_combine_push(PushArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (wv >= a.rows * a.segs)
+        return;
+    const int s = wv / a.segs;
+    const int sg = wv - s * a.segs;
+    if (s >= *a.row_count)
+        return;
+    const int p = a.src_pos[s];
+    if ((unsigned)p >= (unsigned)a.n_pairs)
+        return;
+    const int K = a.topk;
+    const float w = a.weights ? a.weights[(size_t)s * K + p % K] : 1.0f;
+    const int V = a.row_vecs;
+    const u32x4 *row = reinterpret_cast<const u32x4 *>(a.input) + (size_t)s * V;
+    f32x4 *dst = reinterpret_cast<f32x4 *>(a.staging) + (size_t)p * V * 2;
+    u32x4 v[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int j = sg * kWave * CH + lane + kWave * i;
+        if (j < V)
+            v[i] = __builtin_nontemporal_load(row + j);
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int j = sg * kWave * CH + lane + kWave * i;
+        if (j < V) {
+#pragma clang fp contract(off)
+            dst[2 * j] = f32x4{w * bf16_lo(v[i].x), w * bf16_hi(v[i].x), w * bf16_lo(v[i].y),
+                               w * bf16_hi(v[i].y)};
+            dst[2 * j + 1] = f32x4{w * bf16_lo(v[i].z), w * bf16_hi(v[i].z),
+                                   w * bf16_lo(v[i].w), w * bf16_hi(v[i].w)};
+        }
+    }
+}
+
+// Sum of NT staging rows (lane k < NT holds the k-th pair), double buffered.
+template <int NT, int CH>
+__device__ inline void sum_staged(const f32x4 *st, int V, int base, int lane, int my_pair,
+                                  float (&acc)[CH][8])
+{
+    int pr[NT];
+#pragma unroll
+    for (int k = 0; k < NT; ++k)
+        pr[k] = read_lane(my_pair, k);
+    f32x4 buf[2][CH][2];
+    auto load = [&](int p, f32x4 (&d)[CH][2]) {
+        const f32x4 *r = st + (size_t)p * V * 2;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int j = base + lane + kWave * i;
+            if (j < V) {
+                d[i][0] = __builtin_nontemporal_load(r + 2 * j);
+                d[i][1] = __builtin_nontemporal_load(r + 2 * j + 1);
+            } else {
+                d[i][0] = d[i][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        }
+    };
+    load(pr[0], buf[0]);
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+        if (k + 1 < NT)
+            load(pr[k + 1], buf[(k + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+#pragma clang fp contract(off)
+            acc[i][0] = acc[i][0] + buf[k & 1][i][0].x;
+            acc[i][1] = acc[i][1] + buf[k & 1][i][0].y;
+            acc[i][2] = acc[i][2] + buf[k & 1][i][0].z;
+            acc[i][3] = acc[i][3] + buf[k & 1][i][0].w;
+            acc[i][4] = acc[i][4] + buf[k & 1][i][1].x;
+            acc[i][5] = acc[i][5] + buf[k & 1][i][1].y;
+            acc[i][6] = acc[i][6] + buf[k & 1][i][1].z;
+            acc[i][7] = acc[i][7] + buf[k & 1][i][1].w;
+        }
+    }
+}
+
+template <int KT, int CH, int NT = 1>
+__device__ inline void sum_staged_n(int n, const f32x4 *st, int V, int base, int lane,
+                                    int my_pair, float (&acc)[CH][8])
+{
+    if constexpr (NT <= KT) {
+        if (n == NT)
+            sum_staged<NT, CH>(st, V, base, lane, my_pair, acc);
+        else
+            sum_staged_n<KT, CH, NT + 1>(n, st, V, base, lane, my_pair, acc);
+    }
+}
+
+// KT = K known at compile time (double buffered), or 0: runtime K.
+template <int KT, int CH>
+__global__ __launch_bounds__(256) void k_combine_reduce(PushArgs a)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (wv >= a.num_tokens * a.segs)
+        return;
+    const int t = wv / a.segs;
+    const int sg = wv - t * a.segs;
+    const int K = KT > 0 ? KT : a.topk;
+    int my_pair = -1;
+    if (lane < K) {
+        const int p = t * K + lane;
+        const int s = a.slot_of[p];
+        if (s >= 0)
+            my_pair = p;
+        if (a.out_weights && sg == 0)
+            a.out_weights[p] = s < 0 ? 0.0f : (a.weights ? a.weights[(size_t)s * K + lane] : 1.0f);
+    }
+    // pairs with a row to the front lanes, in k order
+    const uint64_t have = __ballot(my_pair >= 0);
+    const int n = __popcll(have);
+    const int r = my_pair >= 0 ? lanes_below(have) : kWave;
+    int cp = -1;
+    for (int j = 0; j < K; ++j) {
+        const int pj = __shfl(my_pair, j, kWave);
+        if (__shfl(r, j, kWave) == lane)
+            cp = pj;
+    }
+    const int V = a.row_vecs;
+    const int base = sg * kWave * CH;
+    float acc[CH][8];
+#pragma unroll
+    for (int i = 0; i < CH; ++i)
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            acc[i][q] = 0.0f;
+    const f32x4 *st = reinterpret_cast<const f32x4 *>(a.staging);
+    if constexpr (KT > 0) {
+        sum_staged_n<KT, CH>(n, st, V, base, lane, cp, acc);
+    } else {
+        for (int k = 0; k < n; ++k)  // one row at a time
+            sum_staged<1, CH>(st, V, base, lane, read_lane(cp, k), acc);
+    }
+    u32x4 *out = reinterpret_cast<u32x4 *>(a.output) + (size_t)t * V;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
         const int j = base + lane + kWave * i;

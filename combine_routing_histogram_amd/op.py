@@ -77,6 +77,7 @@ class EpDispatchCombineOp:
         self._sent_combine = None
         self.u_cap = config.max_tokens * min(config.topk, config.num_ranks)
         self._last_dedup = False
+        self._staging = None
         self._units = None          # unit-row buffers, allocated on first use
         self._unit_carried = (False, False)
 
@@ -256,6 +257,23 @@ class EpDispatchCombineOp:
         self._check_combine(input, weights)
         B.epdc_combine(self._op, self._stream(), _ptr(input), _ptr(weights), _ptr(indices),
                        _ptr(self._combined), _ptr(self._combined_weights))
+        T = self._tokens
+        return self._combined[:T], self._combined_weights[:T]
+
+    def combine_scatter(self, input: torch.Tensor, weights: Optional[torch.Tensor] = None,
+                        indices: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+        """Scatter combine: every received row pushes its weighted fp32 product
+        to a per-(token, k) staging row, then each token adds its K staging
+        rows in k order; same arguments and (bit-identical) result as combine().
+        The fp32 staging rows (max_tokens*topk x hidden) are allocated on
+        first use and kept."""
+        self._check_combine(input, weights)
+        if self._staging is None:
+            self._staging = torch.empty((self.n_cap, self.config.hidden), dtype=torch.float32,
+                                        device=self.device)
+        B.epdc_combine_scatter(self._op, self._stream(), _ptr(input), _ptr(weights),
+                               _ptr(indices), _ptr(self._staging), _ptr(self._combined),
+                               _ptr(self._combined_weights))
         T = self._tokens
         return self._combined[:T], self._combined_weights[:T]
 

@@ -115,7 +115,9 @@ enum {
     EPDC_KERNEL_UNITS_TO_EXPERTS = 6, /* unit rows -> expert rows (conversion) */
     EPDC_KERNEL_EXPERTS_TO_UNITS = 7, /* weighted sum of a unit's expert rows */
     EPDC_KERNEL_COMBINE_UNITS = 8,    /* sum of a token's unit rows */
-    EPDC_NUM_KERNELS = 9
+    EPDC_KERNEL_COMBINE_PUSH = 9,     /* scatter combine: weighted rows -> staging */
+    EPDC_KERNEL_COMBINE_REDUCE = 10,  /* scatter combine: staging -> token rows */
+    EPDC_NUM_KERNELS = 11
 };
 
 /* Bytes of device workspace an op with this config needs (host only, no GPU
@@ -185,6 +187,23 @@ epdc_status epdc_dispatch(epdc_op *op, void *stream, int32_t num_tokens,
 epdc_status epdc_combine(epdc_op *op, void *stream, const void *input,
                          const float *weights, const int32_t *indices,
                          void *output, float *out_weights);
+
+/*
+ * Scatter combine ("Choosing an EP API and backend" page, "EP paths" table,
+ * FlyDSL row: gather/scatter combine).  Reading implemented here: the expert
+ * side pushes each received row, multiplied by its weight in fp32, to the
+ * fp32 staging row of the (token, k) pair it came from, and the token side
+ * adds its K staging rows in k order.  No two rows share a staging row, so no
+ * atomics are needed and the result is bit-identical to epdc_combine (same
+ * products, same order).  Arguments as epdc_combine, plus staging: caller
+ * device memory of max_tokens * topk rows of hidden fp32 values (16-byte
+ * aligned); it holds the weighted products afterwards.  On one GPU this
+ * moves 8 more bytes per element than the gather; it is the form a push
+ * across GPUs would take.
+ */
+epdc_status epdc_combine_scatter(epdc_op *op, void *stream, const void *input,
+                                 const float *weights, const int32_t *indices,
+                                 float *staging, void *output, float *out_weights);
 
 /*
  * Rank-deduplicated dispatch and the standard-MoE conversion.

@@ -107,7 +107,8 @@ def test_kernel_names(lib):
     names = [B.epdc_kernel_name(k) for k in range(B.EPDC_NUM_KERNELS)]
     assert names == ["k_route_rank", "k_route_scan", "k_scatter_copy", "k_scatter_fp8",
                      "k_scatter_mxfp4", "k_combine", "k_units_to_experts",
-                     "k_experts_to_units", "k_combine_units"]
+                     "k_experts_to_units", "k_combine_units", "k_combine_push",
+                     "k_combine_reduce"]
     assert B.epdc_kernel_name(B.EPDC_NUM_KERNELS) is None
 
 
