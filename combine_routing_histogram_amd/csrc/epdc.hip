@@ -240,9 +240,9 @@ ScatterPlan make_plan(int ch, int row_vecs, int max_segs)
 ScatterPlan plan_scatter(int quant, int tokens, int row_vecs, bool inline_route)
 {
     switch (quant) {
-    case EPDC_QUANT_FP8_E4M3_B128:
-        return make_plan(1, row_vecs, 1 << 20);
-    case EPDC_QUANT_MXFP4_B32:
+    case EPDC_QUANT_FP8_E4M3_B128:  // 2 adjacent vectors per lane per pass
+        return make_plan(kFp8PassVecs / kWave, row_vecs, 1 << 20);
+    case EPDC_QUANT_MXFP4_B32:      // 2 vectors per lane per pass
         return make_plan(2, row_vecs, 1 << 20);
     default:
         return tokens >= 2048 && !inline_route ? make_plan(8, row_vecs, 1)
@@ -302,13 +302,13 @@ epdc_status launch_scatter(epdc_op *op, hipStream_t st, ScatterArgs &sa, int mod
     case EPDC_QUANT_FP8_E4M3_B128:
         return launch(op, st, EPDC_KERNEL_SCATTER_FP8, [&] {
             switch (mode) {
-            case kRouteInline: k_scatter_fp8<1, kRouteInline><<<grid, block, 0, st>>>(sa); break;
-            case kRouteReplay: k_scatter_fp8<1, kRouteReplay><<<grid, block, 0, st>>>(sa); break;
-            case kRouteUnits: k_scatter_fp8<1, kRouteUnits><<<grid, block, 0, st>>>(sa); break;
+            case kRouteInline: k_scatter_fp8<kRouteInline><<<grid, block, 0, st>>>(sa); break;
+            case kRouteReplay: k_scatter_fp8<kRouteReplay><<<grid, block, 0, st>>>(sa); break;
+            case kRouteUnits: k_scatter_fp8<kRouteUnits><<<grid, block, 0, st>>>(sa); break;
             case kRouteUnitsReplay:
-                k_scatter_fp8<1, kRouteUnitsReplay><<<grid, block, 0, st>>>(sa);
+                k_scatter_fp8<kRouteUnitsReplay><<<grid, block, 0, st>>>(sa);
                 break;
-            default: k_scatter_fp8<1><<<grid, block, 0, st>>>(sa); break;
+            default: k_scatter_fp8<><<<grid, block, 0, st>>>(sa); break;
             }
         });
     case EPDC_QUANT_MXFP4_B32:
