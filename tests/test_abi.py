@@ -129,3 +129,25 @@ def test_product_code_never_touches_the_oracle():
                                      flags=re.M), f
     hdr = open(os.path.join(ROOT, "include", "epdc.h")).read()
     assert "oracle" not in hdr
+
+
+def test_every_entry_point_rejects_a_null_op(lib):
+    calls = [
+        lambda: B.epdc_dispatch_replay(0, 0, 1, 0, 0, 1, 0, 0),
+        lambda: B.epdc_dispatch_send(0, 0, 1, 1, 0, 0, 1, 1, 0, 0, 0, 1),
+        lambda: B.epdc_dispatch_recv(0, 0),
+        lambda: B.epdc_combine_send(0, 0, 1, 0, 0, 1, 0),
+        lambda: B.epdc_combine_recv(0, 0),
+        lambda: B.epdc_combine_scatter(0, 0, 1, 0, 0, 1, 1, 0),
+        lambda: B.epdc_dispatch_dedup(0, 0, 1, 1, 0, 0, 1, 1, 0, 0, 0, 1),
+        lambda: B.epdc_get_unit_routing(0),
+        lambda: B.epdc_units_to_experts(0, 0, 1, 0, 0, 0, 1, 0, 0, 0),
+        lambda: B.epdc_experts_to_units(0, 0, 1, 0, 1),
+        lambda: B.epdc_combine_units(0, 0, 1, 0, 1, 0),
+        lambda: B.epdc_get_routing(0),
+        lambda: B.epdc_get_dispatch_src_token_pos(0),
+    ]
+    for call in calls:
+        with pytest.raises(B.EpdcError) as ei:
+            call()
+        assert ei.value.status == B.EPDC_ERR_INVALID_ARGS
