@@ -69,3 +69,106 @@ def test_graph_replay_matches_eager(name, tokens):
         got = [g_out[:n].view(torch.uint8), g_recv, g_y, g_yw, op.get_dispatch_src_token_pos()[:n]]
         for a, b in zip(got, ref):
             assert torch.equal(a, b), f"replay {rep} differs from the eager step"
+
+
+def _replay_matches(step, clobber, n_rep=3):
+    """Run `step` eagerly, capture it, and check every replay (with the
+    outputs clobbered by eager work in between) against the eager result."""
+    ref = [t.clone() for t in step()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = step()
+    torch.cuda.synchronize()
+    for rep in range(n_rep):
+        for t in outs:
+            clobber(t)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep} differs"
+
+
+def _clobber(t):
+    t.view(torch.uint8).fill_(0x5A)
+
+
+@pytest.mark.parametrize("name,tokens", [("decode_bf16", None), ("deepseek_v3_bf16", 1024),
+                                         ("qwen3_moe_mxfp4", 300)])
+def test_graph_replay_dedup_pipeline(name, tokens):
+    w = wl.WORKLOADS[name]
+    print(f"graph dedup {name} tokens={tokens}", flush=True)
+    inp = wl.make_inputs(w, tokens=tokens, with_combine_input=True)
+    T = inp["x"].shape[0]
+    x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(DEV)
+    idx = torch.from_numpy(inp["indices"]).to(DEV)
+    wts = torch.from_numpy(inp["weights"]).to(DEV)
+    c_in = torch.from_numpy(inp["combine_input"].view(np.int16)).view(torch.bfloat16).to(DEV)
+    op = EpDispatchCombineOp(EpDispatchCombineConfig(T, w.hidden, w.topk, w.experts, w.ranks,
+                                                     quant=w.quant), DEV)
+
+    _, _, _, _, recv = op.dispatch_dedup(x, wts, None, idx)
+    torch.cuda.synchronize()
+    U = int(recv.sum())
+    n = int(op.get_routing()[0][-1])
+
+    def step():  # only the rows a step writes are compared
+        u_out, u_w, _, _, recv = op.dispatch_dedup(x, wts, None, idx)
+        e_out, e_w, _, _, _ = op.units_to_experts()
+        part = op.experts_to_units(c_in, e_w)
+        y, y_w = op.combine_units(None, u_w)
+        return [recv, u_out[:U], e_out[:n], part[:U], y, y_w]
+
+    _replay_matches(step, _clobber)
+
+
+def test_graph_replay_scatter_combine():
+    w = wl.WORKLOADS["deepseek_v3_bf16"]
+    print("graph scatter combine", flush=True)
+    inp = wl.make_inputs(w, tokens=900)
+    T = inp["x"].shape[0]
+    x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(DEV)
+    idx = torch.from_numpy(inp["indices"]).to(DEV)
+    wts = torch.from_numpy(inp["weights"]).to(DEV)
+    op = EpDispatchCombineOp(EpDispatchCombineConfig(T, w.hidden, w.topk, w.experts, w.ranks),
+                             DEV)
+
+    _, _, _, _, recv = op.dispatch(x, wts, None, idx)
+    torch.cuda.synchronize()
+    n = int(recv.sum())
+
+    def step():
+        out, out_w, _, out_idx, _ = op.dispatch(x, wts, None, idx)
+        y, y_w = op.combine_scatter(out, out_w, out_idx)
+        return [out[:n], y, y_w]
+
+    _replay_matches(step, _clobber)
+
+
+def test_graph_replay_routing_replay():
+    w = wl.WORKLOADS["deepseek_v3_fp8"]
+    print("graph routing replay", flush=True)
+    inp = wl.make_inputs(w, tokens=700, with_combine_input=True)
+    T = inp["x"].shape[0]
+    x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(DEV)
+    x2 = (x.float() * 1.5).to(torch.bfloat16)
+    idx = torch.from_numpy(inp["indices"]).to(DEV)
+    wts = torch.from_numpy(inp["weights"]).to(DEV)
+    op = EpDispatchCombineOp(EpDispatchCombineConfig(T, w.hidden, w.topk, w.experts, w.ranks,
+                                                     quant=w.quant), DEV)
+    _, _, _, _, recv = op.dispatch(x, wts, None, idx)
+    torch.cuda.synchronize()
+    n = int(recv.sum())
+
+    def step():
+        out, out_w, out_s, _, _ = op.dispatch_replay(x2, wts)
+        return [out[:n], out_w[:n], out_s[:n]]
+
+    _replay_matches(step, _clobber)
