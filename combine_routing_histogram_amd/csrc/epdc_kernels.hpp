@@ -429,6 +429,7 @@ struct ScatterArgs {
     const int32_t *row_count;          // device count of input rows (units), or NULL
     int32_t unit_rows_max;             // num_tokens * min(K, R): every unit row is below
     int32_t num_src_tokens;            // tokens of the recorded dispatch (conversion)
+    int32_t tiles;                     // routing tiles (kRouteTableScan)
 };
 
 // ---- inline routing for a single tile (num_tokens * K <= kRouteTile) ----
@@ -578,8 +579,123 @@ enum {
     kRouteReplay = 2,  // slot_of of a dispatch recorded earlier (routing replay)
     kRouteUnits = 3,        // rank-deduplicated: one row per (token, rank), from the unit table
     kRouteConvert = 4,      // a wave per unit row: its pairs' expert rows (standard-MoE layout)
-    kRouteUnitsReplay = 5   // unit rows of a rank-deduplicated dispatch recorded earlier
+    kRouteUnitsReplay = 5,  // unit rows of a rank-deduplicated dispatch recorded earlier
+    kRouteTableScan = 6     // tile histograms scanned by each block (no scan launch)
 };
+
+// ---- the scan folded into the scatter, for small tile tables ----
+//
+// Each block turns the tile histograms k_route_rank wrote into the bases of
+// the (at most two) tiles its tokens fall in: expert totals summed over all
+// tiles, their exclusive scan, plus the counts of the earlier tiles.  Every
+// block reads the whole table, so the host uses this only while the table
+// is small; it saves the one-block scan launch.
+// Largest tile table (tiles x experts entries) the scatter blocks scan, and
+// the most table entries all blocks of one launch may read together.
+constexpr int kFusedScanMaxEntries = 8192;
+constexpr int64_t kFusedScanMaxReads = int64_t(1) << 24;
+
+struct ScanLds {
+    int32_t base[2][kMaxExperts];
+    int32_t eoff[kMaxExperts + 1];
+};
+
+__device__ inline ScanLds &scan_lds()
+{
+    __shared__ ScanLds l;
+    return l;
+}
+
+__device__ inline void block_tile_bases(const ScatterArgs &a, ScanLds &l, int tile0)
+{
+    const int E = a.num_experts;
+    const int B = a.tiles;
+    const int nthr = blockDim.x;
+    for (int e = threadIdx.x; e < E; e += nthr) {
+        int total = 0, pre = 0, c0 = 0;
+        for (int b0 = 0; b0 < B; b0 += 8) {  // 8 independent loads in flight
+            int c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                c[i] = b0 + i < B ? a.tile_table[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                total += c[i];
+                if (b0 + i < tile0)
+                    pre += c[i];
+                else if (b0 + i == tile0)
+                    c0 = c[i];
+            }
+        }
+        l.eoff[e] = total;
+        l.base[0][e] = pre;
+        l.base[1][e] = pre + c0;
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {  // exclusive scan of the totals by one wave
+        const int lane = threadIdx.x;
+        const int per = (E + kWave - 1) / kWave;
+        const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
+        int sum = 0;
+        for (int e = e0; e < e1; ++e)
+            sum += l.eoff[e];
+        int incl = sum;
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int v = __shfl_up(incl, d, kWave);
+            if (lane >= d)
+                incl += v;
+        }
+        int run = incl - sum;
+        for (int e = e0; e < e1; ++e) {
+            const int c = l.eoff[e];
+            l.eoff[e] = run;
+            run += c;
+        }
+        if (lane == kWave - 1)
+            l.eoff[E] = incl;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += nthr) {
+        l.base[0][e] += l.eoff[e];
+        l.base[1][e] += l.eoff[e];
+    }
+    if (blockIdx.x == 0) {  // publish the offsets and the counts
+        const int R = a.num_ranks;
+        const int per_rank = E / R;
+        for (int e = threadIdx.x; e <= E; e += nthr)
+            a.expert_off[e] = l.eoff[e];
+        for (int r = threadIdx.x; r <= R; r += nthr)
+            a.rank_off[r] = l.eoff[r * per_rank];
+        for (int r = threadIdx.x; r < R; r += nthr)
+            a.recv_count[r] = l.eoff[(r + 1) * per_rank] - l.eoff[r * per_rank];
+    }
+    __syncthreads();
+}
+
+// Slot of this lane's pair from the block's bases (tile0 = the block's first tile).
+__device__ inline int pair_slot_scan(const ScatterArgs &a, const ScanLds &l, int tile0, int t,
+                                     int lane, bool record)
+{
+    int s = -1;
+    if (lane < a.topk) {
+        const int p = t * a.topk + lane;
+        const int r = a.rank_in_tile[p];
+        if (r >= 0) {
+            const int e = a.indices[p];
+            s = l.base[p / kRouteTile - tile0][e] + r;
+            if ((unsigned)s >= (unsigned)a.n_pairs) {
+                if (record)
+                    atomicOr(&a.ctrl[kCtrlError], 2u);
+                s = -1;
+            } else if (record) {
+                a.src_pos[s] = p;
+            }
+        }
+        if (record)
+            a.slot_of[p] = s;
+    }
+    return s;
+}
 
 // Rank-deduplicated dispatch: the pair's expert slot is recorded as in
 // kRouteTable (the conversion and the combine use it), and the wave writes
@@ -654,6 +770,13 @@ __device__ inline void route_wave(const ScatterArgs &a, bool has_work, int seg, 
         inline_route(a, l);
         if (has_work)
             w.slot = pair_slot_inline(a, l, w.t, w.lane, seg == 0);
+    } else if constexpr (MODE == kRouteTableScan) {
+        // every wave of the block takes part in the block's scan
+        ScanLds &l = scan_lds();
+        const int tile0 = (int)(((int64_t)blockIdx.x * a.work_waves / a.segs) * a.topk / kRouteTile);
+        block_tile_bases(a, l, tile0);
+        if (has_work)
+            w.slot = pair_slot_scan(a, l, tile0, w.t, w.lane, seg == 0);
     } else if constexpr (MODE == kRouteUnits) {
         if (has_work) {  // wave-uniform: the shuffles in unit_slot see the whole wave
             if (seg == 0)

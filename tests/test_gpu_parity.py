@@ -373,20 +373,38 @@ def test_single_tile_dispatch_is_one_launch():
     assert set(prof) == {"k_scatter_copy", "k_combine"}
 
 
-def test_profile_events_time_every_kernel():
-    log("profile events")
-    w = wl.WORKLOADS["deepseek_v3_bf16"]
-    inp = inputs_for("deepseek_v3_bf16", 1024)
-    op = EpDispatchCombineOp(EpDispatchCombineConfig(1024, w.hidden, w.topk, w.experts,
-                                                     w.ranks), DEV)
+# tiles x experts <= 8192: the scatter blocks scan the tile table themselves;
+# larger tables take the one-block scan launch
+@pytest.mark.parametrize("name,tokens,kernels", [
+    ("deepseek_v3_bf16", 1024, {"k_route_rank", "k_scatter_copy", "k_combine"}),
+    ("qwen3_moe_mxfp4", 9000, {"k_route_rank", "k_route_scan", "k_scatter_mxfp4", "k_combine"}),
+])
+def test_profile_events_time_every_kernel(name, tokens, kernels):
+    log(f"profile events {name}")
+    w = wl.WORKLOADS[name]
+    inp = inputs_for(name, tokens)
+    op = EpDispatchCombineOp(EpDispatchCombineConfig(tokens, w.hidden, w.topk, w.experts,
+                                                     w.ranks, quant=w.quant), DEV)
     x = bf16_dev(inp["x"])
     idx = torch.from_numpy(inp["indices"]).to(DEV)
     wt = torch.from_numpy(inp["weights"]).to(DEV)
+    c_in = bf16_dev(inp["combine_input"])
     op.profile_begin(16)
     for _ in range(3):
         out, out_w, _, out_idx, _ = op.dispatch(x, wt, None, idx)
-        op.combine(out, out_w, out_idx)
+        op.combine(out if w.quant == "none" else c_in, out_w, out_idx)
     prof = op.profile_end()
-    assert set(prof) == {"k_route_rank", "k_route_scan", "k_scatter_copy", "k_combine"}
-    for name, (ms, n) in prof.items():
-        assert n == 3 and ms > 0, name
+    assert set(prof) == kernels
+    for k, (ms, n) in prof.items():
+        assert n == 3 and ms > 0, k
+
+
+def test_scatter_blocks_straddling_two_tiles():
+    """4 tokens x 6 pairs per block: blocks cross tile boundaries, so the
+    blocks' own scan must give the second tile's bases too."""
+    log("straddling blocks")
+    rng = np.random.default_rng(25)
+    T, H, K, E, R = 4096, 256, 6, 96, 3
+    x = wl.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    idx = wl.draw_topk(rng, T, E, K, "zipf", 1.1)
+    run_case(x, wl.softmax_weights(rng, T, K), idx, E, R)
