@@ -8,7 +8,7 @@ JSON with the hash of the kernel source it was measured on, so a reader can
 tell when the figure has gone stale.
 
     python -m combine_routing_histogram_amd.profiling traffic \\
-        --fetch-dir gpurun_out/pmc_fetch --write-dir gpurun_out/pmc_write \\
+        --fetch-dir prof/pmc_fetch --write-dir prof/pmc_write \\
         --kernel k_combine --workload deepseek_v3_bf16 --calib-bytes 536870912 \\
         --out profiles/traffic_k_combine_deepseek_v3_bf16.json
 """
