@@ -48,6 +48,7 @@ struct Layout {
     size_t ctrl, tile_table, rank_in_tile, expert_off, rank_off, slot_of, src_pos;
     // rank-deduplicated dispatch: the unit routing and the pairs' rank counts
     size_t unit_table, unit_rank_in_tile, unit_off, unit_of, unit_src, pair_recv;
+    size_t tile_cnt16;  // [E][<= 8 * kScanMaxLoads] 16-bit tile counts
     size_t total;
     int64_t n_cap;
     int64_t u_cap;  // max_tokens * min(topk, num_ranks)
@@ -134,6 +135,8 @@ Layout layout_for(const epdc_config &c)
     off += align256(sizeof(int32_t) * (size_t)l.u_cap);
     l.pair_recv = off;
     off += align256(sizeof(int32_t) * (size_t)c.num_ranks);
+    l.tile_cnt16 = off;
+    off += align256(sizeof(uint16_t) * 8 * kScanMaxLoads * (size_t)c.num_experts);
     l.total = off;
     return l;
 }
@@ -578,10 +581,13 @@ epdc_status dispatch_impl(epdc_op *op, void *stream, int32_t num_tokens, const v
     // A small tile table is scanned by every scatter block instead of a scan
     // launch, while all blocks together read at most kFusedScanMaxReads
     // entries: 32 tiles x 256 experts over the 1024 blocks of the bf16 copy
-    // at 4096 tokens saves 2.7 us per dispatch, the same table over the 7168
-    // blocks of the FP8 scatter costs 9 us.
+    // at 4096 tokens saves about 2 us per dispatch, the same table over the
+    // 7168 blocks of the FP8 scatter costs 9-23 us.
     bool fused_scan = false;
-    if (!dedup && tiles > 1 && (int64_t)tiles * c.num_experts <= kFusedScanMaxEntries) {
+    if (!dedup && tiles > 1 && tiles <= 8 * kScanMaxLoads &&
+        (int64_t)tiles * c.num_experts <= kFusedScanMaxEntries) {
+        // the per-block scan costs each block a few us of latency: only
+        // worth it while the scatter has few blocks
         const int in_vecs = c.quant == EPDC_QUANT_NONE
                                 ? (c.input_kind == EPDC_IN_RAW ? c.raw_row_bytes / 16 : c.hidden / 8)
                                 : c.hidden / 8;
@@ -591,6 +597,9 @@ epdc_status dispatch_impl(epdc_op *op, void *stream, int32_t num_tokens, const v
         const int64_t blocks = (waves + wpb - 1) / wpb;
         fused_scan = blocks * tiles * c.num_experts <= kFusedScanMaxReads;
     }
+    const int tiles_pad8 = (tiles + 7) & ~7;
+    ra.tile_cnt16 = fused_scan ? reinterpret_cast<uint16_t *>(op->ws + op->lay.tile_cnt16) : nullptr;
+    ra.tiles_pad8 = tiles_pad8;
     if (dedup) {
         // the unit level: keys = destination ranks of the pairs that open a
         // unit; its offsets are both the expert and the rank offsets (one key
@@ -685,6 +694,8 @@ epdc_status dispatch_impl(epdc_op *op, void *stream, int32_t num_tokens, const v
     }
 
     sa.tiles = tiles;
+    sa.tile_cnt16 = ra.tile_cnt16;
+    sa.tiles_pad8 = tiles_pad8;
     s = launch_scatter(op, st, sa,
                        dedup ? kRouteUnits
                              : (inline_route ? kRouteInline

@@ -99,6 +99,8 @@ struct RouteArgs {
     int32_t key_div;         // 0: the key is the expert id; > 0: unit keys (below)
     int32_t tiles;           // ceil(n_pairs / kRouteTile), >= 1
     int32_t *tile_table;     // [tiles][E]: counts, then first slot per (tile, e)
+    uint16_t *tile_cnt16;    // or NULL; else [E][tiles_pad8] 16-bit counts (scatter-side scan)
+    int32_t tiles_pad8;      // tiles rounded up to a multiple of 8
     int32_t *rank_in_tile;   // [n_pairs], -1 for an invalid id
     int32_t *expert_off;     // [E+1]
     int32_t *rank_off;       // [R+1]
@@ -269,8 +271,19 @@ __device__ inline void route_rank_body(const RouteArgs &a)
     if (p < a.n_pairs)
         a.rank_in_tile[p] = r.rank;
     if (!SINGLE_TILE) {
-        if (tid < E)
+        if (a.tile_cnt16) {
+            // by expert, 16 bits per tile (a tile holds at most 1024 pairs):
+            // the scatter blocks read one expert's tiles with 16-byte loads
+            if (tid < E) {
+                uint16_t *row = a.tile_cnt16 + (size_t)tid * a.tiles_pad8;
+                row[tile] = (uint16_t)r.col_total;
+                if (tile == a.tiles - 1)
+                    for (int b = a.tiles; b < a.tiles_pad8; ++b)
+                        row[b] = 0;
+            }
+        } else if (tid < E) {
             a.tile_table[(size_t)tile * E + tid] = r.col_total;
+        }
     } else {
         // the only tile: its histogram is the whole histogram
         write_offsets(E, a.num_ranks, r.col_total, eoff, s_wave_tot, a.expert_off, a.rank_off,
@@ -430,6 +443,8 @@ struct ScatterArgs {
     int32_t unit_rows_max;             // num_tokens * min(K, R): every unit row is below
     int32_t num_src_tokens;            // tokens of the recorded dispatch (conversion)
     int32_t tiles;                     // routing tiles (kRouteTableScan)
+    const uint16_t *tile_cnt16;        // [E][tiles_pad8] tile counts (kRouteTableScan)
+    int32_t tiles_pad8;
 };
 
 // ---- inline routing for a single tile (num_tokens * K <= kRouteTile) ----
@@ -594,6 +609,7 @@ enum {
 // the most table entries all blocks of one launch may read together.
 constexpr int kFusedScanMaxEntries = 8192;
 constexpr int64_t kFusedScanMaxReads = int64_t(1) << 24;
+constexpr int kScanMaxLoads = 8;  // 16-byte loads per expert row: at most 64 tiles
 
 struct ScanLds {
     int32_t base[2][kMaxExperts];
@@ -609,22 +625,27 @@ __device__ inline ScanLds &scan_lds()
 __device__ inline void block_tile_bases(const ScatterArgs &a, ScanLds &l, int tile0)
 {
     const int E = a.num_experts;
-    const int B = a.tiles;
     const int nthr = blockDim.x;
+    const int n16 = a.tiles_pad8 / 8;  // 16-byte loads per expert row (<= kScanMaxLoads)
     for (int e = threadIdx.x; e < E; e += nthr) {
+        const u32x4 *row = reinterpret_cast<const u32x4 *>(a.tile_cnt16 + (size_t)e * a.tiles_pad8);
+        u32x4 v[kScanMaxLoads];
+#pragma unroll
+        for (int j = 0; j < kScanMaxLoads; ++j)  // independent loads in flight
+            v[j] = j < n16 ? row[j] : u32x4{0u, 0u, 0u, 0u};
         int total = 0, pre = 0, c0 = 0;
-        for (int b0 = 0; b0 < B; b0 += 8) {  // 8 independent loads in flight
-            int c[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                c[i] = b0 + i < B ? a.tile_table[(size_t)(b0 + i) * E + e] : 0;
+        for (int j = 0; j < kScanMaxLoads; ++j) {
+            const uint32_t wd[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                total += c[i];
-                if (b0 + i < tile0)
-                    pre += c[i];
-                else if (b0 + i == tile0)
-                    c0 = c[i];
+            for (int h = 0; h < 8; ++h) {
+                const int c = (int)((wd[h >> 1] >> (16 * (h & 1))) & 0xFFFFu);
+                const int b = 8 * j + h;
+                total += c;
+                if (b < tile0)
+                    pre += c;
+                else if (b == tile0)
+                    c0 = c;
             }
         }
         l.eoff[e] = total;
