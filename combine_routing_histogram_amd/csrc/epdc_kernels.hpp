@@ -84,10 +84,11 @@ __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0
 // count, the first slot of that expert's run inside that tile.  Slot of pair
 // p = table[tile(p)][e] + rank_in_tile[p]: experts ascending, pairs in
 // ascending p inside an expert.  With a single tile the rank kernel scans its
-// own histogram and the second launch is skipped.  The kernel boundary is the
-// only cross-block synchronization: an in-kernel "last block scans" scheme
-// needs agent-scope fences, i.e. L2 writeback/invalidate across the XCDs, and
-// measured slower than the second launch.
+// own histogram and the second launch is skipped; with a small table the
+// scatter blocks scan it themselves (kRouteTableScan below).  The kernel
+// boundary is the only cross-block synchronization: an in-kernel "last block
+// scans" scheme needs agent-scope fences, i.e. L2 writeback/invalidate across
+// the XCDs, and measured slower than the second launch.
 
 struct RouteArgs {
     const int32_t *indices;  // [n_pairs]
@@ -394,11 +395,11 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scan2(RouteArgs a, Rout
 // Dispatch scatter: one wave per (token, row segment)
 // ---------------------------------------------------------------------------
 //
-// A wave owns a segment of one token row (seg_vecs 16-byte input vectors,
-// CH per lane per pass): it reads each vector once, quantizes it if asked,
-// and writes it to the token's K received rows.  Several waves per token keep the grid
-// many waves deep, so the kernel is bound by HBM throughput rather than by
-// the latency of one wave walking a whole row.  Every wave of a token derives
+// A wave owns a segment of one token row (seg_vecs 16-byte input vectors, a
+// whole number of passes): it reads each vector once, quantizes it if asked,
+// and writes it to the token's K received rows.  Several waves per token keep
+// the grid many waves deep, so the kernel is bound by HBM throughput rather
+// than by the latency of one wave walking a whole row.  Every wave of a token derives
 // the same K slots; the wave of segment 0 records them and carries the small
 // per-slot rows (weights, indices, scales).
 

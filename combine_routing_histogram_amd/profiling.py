@@ -28,8 +28,29 @@ KERNEL_SRC = os.path.join(PKG, "csrc", "epdc_kernels.hpp")
 CALIB_PATTERNS = ("copyBuffer", "elementwise")
 
 
-def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def _code_only(text: str) -> str:
+    """The kernel source without comments and blank space, so that a comment
+    edit does not mark counter figures as stale (string literals hold no
+    comment markers in this file)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def kernel_source_hash(text: str = None) -> str:
+    """Hash of the kernel code (comments and spacing ignored)."""
+    if text is None:
+        text = open(KERNEL_SRC).read()
+    return hashlib.sha256(_code_only(text).encode()).hexdigest()[:16]
 
 
 def read_counters(run_dir: str, counter: str) -> Dict[str, List[float]]:
