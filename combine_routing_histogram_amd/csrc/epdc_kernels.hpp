@@ -1077,71 +1077,6 @@ enum {
     kCombineUnitsOut = 2   // token t: its distinct unit rows in ascending order, unweighted
 };
 
-// Lane k's (row, weight) term of the wave's sum, k = 0..K-1 in summation
-// order (-1: none); also writes the returned weights where the mode has them.
-template <int MODE>
-__device__ inline void combine_terms(const CombineArgs &a, int row, int sg, int lane, int K,
-                                     int &my_slot, float &my_w)
-{
-    my_slot = -1;
-    my_w = 0.0f;
-    if constexpr (MODE == kCombinePairs) {
-        if (lane < K) {
-            const int p = row * K + lane;
-            my_slot = a.slot_of[p];
-            if (my_slot >= 0)
-                my_w = a.weights ? a.weights[(size_t)my_slot * K + lane] : 1.0f;
-            if (a.out_weights && sg == 0)
-                a.out_weights[p] = my_w;
-        }
-    } else if constexpr (MODE == kCombineUnitsIn) {
-        if (lane < K) {
-            const int t = a.unit_src[row];
-            if ((unsigned)t < (unsigned)a.num_src_tokens) {
-                const int p = t * K + lane;
-                const int s = a.slot_of[p];
-                if (a.unit_of[p] == row && (unsigned)s < (unsigned)a.n_pairs) {
-                    my_slot = s;
-                    my_w = a.weights ? a.weights[(size_t)s * K + lane] : 1.0f;
-                }
-            }
-        }
-    } else {
-        int u = -1;
-        if (lane < K) {
-            u = a.unit_of[row * K + lane];
-            if ((unsigned)u >= (unsigned)a.in_rows_max)
-                u = -1;
-            if (a.out_weights && sg == 0)
-                a.out_weights[row * K + lane] =
-                    u < 0 ? 0.0f : (a.weights ? a.weights[(size_t)u * K + lane] : 1.0f);
-        }
-        // the first lane holding a unit opens it; openers are ordered by unit row
-        int opener = u >= 0;
-        for (int j = 0; j < K; ++j) {
-            const int uj = __shfl(u, j, kWave);
-            if (j < lane && uj == u)
-                opener = 0;
-        }
-        int pos = 0;
-        for (int j = 0; j < K; ++j) {
-            const int uj = __shfl(u, j, kWave);
-            const int oj = __shfl(opener, j, kWave);
-            if (oj && uj < u)
-                ++pos;
-        }
-        for (int j = 0; j < K; ++j) {
-            const int uj = __shfl(u, j, kWave);
-            const int oj = __shfl(opener, j, kWave);
-            const int pj = __shfl(pos, j, kWave);
-            if (oj && pj == lane) {
-                my_slot = uj;
-                my_w = 1.0f;  // 1 * x is x: the sum is that of the unit rows
-            }
-        }
-    }
-}
-
 __device__ inline uint32_t pack_bf16_rne(float lo, float hi)
 {
     const bf16x2 b = __builtin_convertvector(f32x2{lo, hi}, bf16x2);  // v_cvt_pk_bf16_f32
@@ -1161,6 +1096,77 @@ __device__ inline void accumulate_row(float *acc, float w, u32x4 x)
     acc[7] = acc[7] + w * bf16_hi(x.w);
 }
 
+// The wave's terms in summation order, compacted to the front lanes: lane
+// i < n holds the input row (cs) of the i-th term and the index k of its pair
+// (ck); n is wave-uniform.  Pairs and units-in terms are the token's pairs in
+// k order that have a row (terms without one add nothing); units-out terms
+// are the token's distinct unit rows, ascending.  Also writes the returned
+// weights that need no term weight (missing pairs, units-out).  Cross-lane
+// reads use v_readlane (the lane index is uniform), not LDS permutes.
+template <int MODE>
+__device__ inline int combine_slots(const CombineArgs &a, int row, int sg, int lane, int K,
+                                    int &cs, int &ck)
+{
+    cs = -1;
+    ck = 0;
+    if constexpr (MODE == kCombineUnitsOut) {
+        int u = -1;
+        if (lane < K) {
+            u = a.unit_of[row * K + lane];
+            if ((unsigned)u >= (unsigned)a.in_rows_max)
+                u = -1;
+            if (a.out_weights && sg == 0)
+                a.out_weights[row * K + lane] =
+                    u < 0 ? 0.0f : (a.weights ? a.weights[(size_t)u * K + lane] : 1.0f);
+        }
+        // the first lane holding a unit opens it; openers are ordered by unit row
+        int opener = u >= 0;
+        for (int j = 0; j < K; ++j)
+            if (j < lane && read_lane(u, j) == u)
+                opener = 0;
+        int pos = 0;
+        for (int j = 0; j < K; ++j)
+            if (read_lane(opener, j) && read_lane(u, j) < u)
+                ++pos;
+        for (int j = 0; j < K; ++j)
+            if (read_lane(opener, j) && read_lane(pos, j) == lane) {
+                cs = read_lane(u, j);
+                ck = j;
+            }
+        return __popcll(__ballot(opener));
+    } else {
+        int s = -1;
+        if (lane < K) {
+            if constexpr (MODE == kCombinePairs) {
+                s = a.slot_of[row * K + lane];
+            } else {
+                const int t = a.unit_src[row];
+                if ((unsigned)t < (unsigned)a.num_src_tokens) {
+                    const int p = t * K + lane;
+                    const int s0 = a.slot_of[p];
+                    if (a.unit_of[p] == row && (unsigned)s0 < (unsigned)a.n_pairs)
+                        s = s0;
+                }
+            }
+            if (MODE == kCombinePairs && s < 0 && a.out_weights && sg == 0)
+                a.out_weights[row * K + lane] = 0.0f;
+        }
+        const uint64_t have = __ballot(s >= 0);
+        if (have == (uint64_t(1) << K) - 1) {  // every pair has a row: already compact
+            cs = s;
+            ck = lane;
+        } else {
+            const int r = s >= 0 ? lanes_below(have) : kWave;
+            for (int j = 0; j < K; ++j)
+                if (read_lane(r, j) == lane) {
+                    cs = read_lane(s, j);
+                    ck = j;
+                }
+        }
+        return __popcll(have);
+    }
+}
+
 // CH vectors per lane of row s's segment starting at vector `base`.
 template <int CH>
 __device__ inline void load_segment(const u32x4 *in, int s, int V, int base, int lane,
@@ -1174,29 +1180,25 @@ __device__ inline void load_segment(const u32x4 *in, int s, int V, int base, int
     }
 }
 
-// Sum of NT rows, lane k < NT holding the k-th slot and weight: the segment
-// of row k+1 loads while row k is accumulated.  NT is a compile-time count so
-// no load sits behind a branch and the wait counters stay exact.
+// Sum of NT rows, lane k < NT holding the k-th slot and weight, all NT rows'
+// segments requested at once.  NT is a compile-time count so no load sits
+// behind a branch and the wait counters stay exact.
 template <int NT, int CH>
 __device__ inline void sum_rows(const u32x4 *in, int V, int base, int lane, int my_slot,
                                 float my_w, float (&acc)[CH][8])
 {
-    int slot[NT];
-    float w[NT];
+    // the rows are requested before the weights are read, so the rows' loads
+    // never wait for the weights' (which depend on the slots)
+    u32x4 buf[NT][CH];
+#pragma unroll
+    for (int k = 0; k < NT; ++k)
+        load_segment<CH>(in, read_lane(my_slot, k), V, base, lane, buf[k]);
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
-        slot[k] = read_lane(my_slot, k);
-        w[k] = read_lane_f(my_w, k);
-    }
-    u32x4 buf[2][CH];
-    load_segment<CH>(in, slot[0], V, base, lane, buf[0]);
-#pragma unroll
-    for (int k = 0; k < NT; ++k) {
-        if (k + 1 < NT)
-            load_segment<CH>(in, slot[k + 1], V, base, lane, buf[(k + 1) & 1]);
+        const float w = read_lane_f(my_w, k);
 #pragma unroll
         for (int i = 0; i < CH; ++i)
-            accumulate_row(acc[i], w[k], buf[k & 1][i]);
+            accumulate_row(acc[i], w, buf[k][i]);
     }
 }
 
@@ -1228,28 +1230,13 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
     if (a.row_count && t >= *a.row_count)
         return;
 
-    int my_slot;
-    float my_w;
-    combine_terms<MODE>(a, t, sg, lane, K, my_slot, my_w);
-    // the terms with a row move to the front lanes, in lane order (the
-    // summation order is unchanged: terms without a row add nothing)
-    const uint64_t have = __ballot(my_slot >= 0);
-    const int n = __popcll(have);
-    if constexpr (MODE != kCombineUnitsOut) {  // units-out terms are already compact
-        const int r = my_slot >= 0 ? lanes_below(have) : kWave;
-        int cs = -1;
-        float cw = 0.0f;
-        for (int j = 0; j < K; ++j) {
-            const int sj = __shfl(my_slot, j, kWave);
-            const float wj = __shfl(my_w, j, kWave);
-            if (__shfl(r, j, kWave) == lane) {
-                cs = sj;
-                cw = wj;
-            }
-        }
-        my_slot = cs;
-        my_w = cw;
-    }
+    int my_slot, my_k;
+    const int n = combine_slots<MODE>(a, t, sg, lane, K, my_slot, my_k);
+    // term weights: requested now, read only after the rows' loads are issued
+    float my_w = 0.0f;
+    if (lane < n)
+        my_w = (MODE == kCombineUnitsOut || !a.weights) ? 1.0f
+                                                        : a.weights[(size_t)my_slot * K + my_k];
     const int V = a.row_vecs;
     const int base = sg * kWave * CH;
     u32x4 *out = reinterpret_cast<u32x4 *>(a.output) + (size_t)t * V;
@@ -1274,6 +1261,9 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
                 accumulate_row(acc[i], wk, buf[i]);
         }
     }
+
+    if (MODE == kCombinePairs && a.out_weights && sg == 0 && lane < n)
+        a.out_weights[t * K + my_k] = my_w;
 
     // Nontemporal output stores: ordinary stores of the output slow this
     // read-dominated kernel down by 10-13% when its input rows come from HBM
