@@ -747,8 +747,8 @@ __device__ inline int unit_slot(const ScatterArgs &a, int t, int lane, bool reco
     // the unit of every pair: the row of the opener on the same rank
     int unit = -1;
     for (int j = 0; j < K; ++j) {
-        const int rj = __shfl(rank, j, kWave);
-        const int uj = __shfl(us, j, kWave);
+        const int rj = read_lane(rank, j);
+        const int uj = read_lane(us, j);
         if (unit < 0 && rank >= 0 && rj == rank && uj >= 0)
             unit = uj;
     }
@@ -818,7 +818,7 @@ __device__ inline void route_wave(const ScatterArgs &a, bool has_work, int seg, 
             }
             int opener = u >= 0;  // the first of the token's pairs in the unit writes it
             for (int j = 0; j < a.topk; ++j) {
-                const int uj = __shfl(u, j, kWave);
+                const int uj = read_lane(u, j);
                 if (j < w.lane && uj == u)
                     opener = 0;
             }
@@ -1121,18 +1121,27 @@ __device__ inline int combine_slots(const CombineArgs &a, int row, int sg, int l
         }
         // the first lane holding a unit opens it; openers are ordered by unit row
         int opener = u >= 0;
-        for (int j = 0; j < K; ++j)
-            if (j < lane && read_lane(u, j) == u)
+        for (int j = 0; j < K; ++j) {
+            const int uj = read_lane(u, j);
+            if (j < lane && uj == u)
                 opener = 0;
+        }
         int pos = 0;
-        for (int j = 0; j < K; ++j)
-            if (read_lane(opener, j) && read_lane(u, j) < u)
+        for (int j = 0; j < K; ++j) {
+            const int oj = read_lane(opener, j);
+            const int uj = read_lane(u, j);
+            if (oj && uj < u)
                 ++pos;
-        for (int j = 0; j < K; ++j)
-            if (read_lane(opener, j) && read_lane(pos, j) == lane) {
-                cs = read_lane(u, j);
+        }
+        for (int j = 0; j < K; ++j) {
+            const int oj = read_lane(opener, j);
+            const int pj = read_lane(pos, j);
+            const int uj = read_lane(u, j);
+            if (oj && pj == lane) {
+                cs = uj;
                 ck = j;
             }
+        }
         return __popcll(__ballot(opener));
     } else {
         int s = -1;
@@ -1157,11 +1166,14 @@ __device__ inline int combine_slots(const CombineArgs &a, int row, int sg, int l
             ck = lane;
         } else {
             const int r = s >= 0 ? lanes_below(have) : kWave;
-            for (int j = 0; j < K; ++j)
-                if (read_lane(r, j) == lane) {
-                    cs = read_lane(s, j);
+            for (int j = 0; j < K; ++j) {
+                const int rj = read_lane(r, j);
+                const int sj = read_lane(s, j);
+                if (rj == lane) {
+                    cs = sj;
                     ck = j;
                 }
+            }
         }
         return __popcll(have);
     }
@@ -1430,8 +1442,8 @@ __global__ __launch_bounds__(256) void k_combine_reduce(PushArgs a)
     const int r = my_pair >= 0 ? lanes_below(have) : kWave;
     int cp = -1;
     for (int j = 0; j < K; ++j) {
-        const int pj = __shfl(my_pair, j, kWave);
-        if (__shfl(r, j, kWave) == lane)
+        const int pj = read_lane(my_pair, j);
+        if (read_lane(r, j) == lane)
             cp = pj;
     }
     const int V = a.row_vecs;

@@ -44,6 +44,16 @@ def _ptr(t: Optional[torch.Tensor]) -> int:
     return 0 if t is None else t.data_ptr()
 
 
+def _raw_stream(device_index: int) -> int:
+    """The current stream of the device as a raw handle."""
+    return torch._C._cuda_getCurrentRawStream(device_index)
+
+
+if not hasattr(torch._C, "_cuda_getCurrentRawStream"):  # older torch
+    def _raw_stream(device_index: int) -> int:  # noqa: F811
+        return torch.cuda.current_stream(device_index).cuda_stream
+
+
 class EpDispatchCombineOp:
     def __init__(self, config: EpDispatchCombineConfig, device: Optional[torch.device] = None):
         self.config = config
@@ -72,6 +82,12 @@ class EpDispatchCombineOp:
             self._op = B.epdc_create(c, self.workspace.data_ptr(), ws_bytes)
         self._tokens = 0
         self._scales_dtype = None
+        self._dev_index = self.device.index if self.device.index is not None else \
+            torch.cuda.current_device()
+        L = B.lib()
+        self._f_dispatch, self._f_combine = L.epdc_dispatch, L.epdc_combine
+        self._payload_v = self._payload_view(self._out)
+        self._combined_cut = {}   # T -> (output view, weights view)
         self._side_stream = None
         self._sent_dispatch = None
         self._sent_combine = None
@@ -91,17 +107,20 @@ class EpDispatchCombineOp:
             self._op = None
 
     # ---- helpers -------------------------------------------------------------------
+    # Host cost matters for small batches (a 128-token step is ~16 us of GPU
+    # time): the stream is read as a raw handle, library functions and buffer
+    # views are looked up once, and the argument checks use cheap accessors.
     def _stream(self) -> int:
-        return torch.cuda.current_stream(self.device).cuda_stream
+        return _raw_stream(self._dev_index)
 
     def _need(self, t: torch.Tensor, name: str, dtype=None, shape=None):
-        if t.device != self.device:
+        if t.get_device() != self._dev_index:
             raise ValueError(f"{name} is on {t.device}, op is on {self.device}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
         if dtype is not None and t.dtype != dtype:
             raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
-        if shape is not None and tuple(t.shape) != tuple(shape):
+        if shape is not None and t.shape != shape:
             raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
     def _ws_view(self, ptr: int, count: int) -> torch.Tensor:
@@ -153,12 +172,15 @@ class EpDispatchCombineOp:
         [N_cap, H] for FP8, uint8 [N_cap, H/2] (packed E2M1) for MXFP4, or
         uint8 [N_cap, raw_row_bytes] for raw rows.
         """
-        T = int(indices.shape[0])
+        T = indices.shape[0]
         self._need(indices, "indices", torch.int32, (T, self.config.topk))
         self._check_payload(input, weights, scales, T)
         i, w, s, o, ow, os_ = self._dispatch_ptrs(input, weights, scales)
-        B.epdc_dispatch(self._op, self._stream(), T, i, w, s, _ptr(indices), o, ow, os_,
-                        _ptr(self._out_indices), _ptr(self._recv_count))
+        st = self._f_dispatch(self._op, _raw_stream(self._dev_index), T, i or None, w or None,
+                              s or None, indices.data_ptr(), o, ow or None, os_ or None,
+                              self._out_indices.data_ptr(), self._recv_count.data_ptr())
+        if st:
+            B._check(st)
         self._tokens = T
         self._last_dedup = False
         return self._dispatch_views(weights, scales)
@@ -241,7 +263,13 @@ class EpDispatchCombineOp:
         return buf.view(self._scales_dtype or torch.uint8)
 
     def received_payload(self) -> torch.Tensor:
-        return self._payload_view(self._out)
+        return self._payload_v
+
+    def _combined_views(self, T: int):
+        v = self._combined_cut.get(T)
+        if v is None:
+            v = self._combined_cut[T] = (self._combined[:T], self._combined_weights[:T])
+        return v
 
     def received_scales(self, carried: bool = True) -> Optional[torch.Tensor]:
         return self._scales_view(self._out_scales, carried)
@@ -255,10 +283,13 @@ class EpDispatchCombineOp:
         the received layout or None.  Returns (output bf16 [T, H], weights fp32 [T, K]).
         """
         self._check_combine(input, weights)
-        B.epdc_combine(self._op, self._stream(), _ptr(input), _ptr(weights), _ptr(indices),
-                       _ptr(self._combined), _ptr(self._combined_weights))
-        T = self._tokens
-        return self._combined[:T], self._combined_weights[:T]
+        st = self._f_combine(self._op, _raw_stream(self._dev_index), input.data_ptr(),
+                             None if weights is None else weights.data_ptr(),
+                             None if indices is None else indices.data_ptr(),
+                             self._combined.data_ptr(), self._combined_weights.data_ptr())
+        if st:
+            B._check(st)
+        return self._combined_views(self._tokens)
 
     def combine_scatter(self, input: torch.Tensor, weights: Optional[torch.Tensor] = None,
                         indices: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
