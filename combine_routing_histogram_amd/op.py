@@ -87,7 +87,7 @@ class EpDispatchCombineOp:
         L = B.lib()
         self._f_dispatch, self._f_combine = L.epdc_dispatch, L.epdc_combine
         self._payload_v = self._payload_view(self._out)
-        self._combined_cut = {}   # T -> (output view, weights view)
+        self._combined_cut = (-1, None)   # (T, (output view, weights view))
         self._side_stream = None
         self._sent_dispatch = None
         self._sent_combine = None
@@ -266,10 +266,9 @@ class EpDispatchCombineOp:
         return self._payload_v
 
     def _combined_views(self, T: int):
-        v = self._combined_cut.get(T)
-        if v is None:
-            v = self._combined_cut[T] = (self._combined[:T], self._combined_weights[:T])
-        return v
+        if self._combined_cut[0] != T:  # the views of the last token count are kept
+            self._combined_cut = (T, (self._combined[:T], self._combined_weights[:T]))
+        return self._combined_cut[1]
 
     def received_scales(self, carried: bool = True) -> Optional[torch.Tensor]:
         return self._scales_view(self._out_scales, carried)
