@@ -151,3 +151,21 @@ def test_every_entry_point_rejects_a_null_op(lib):
         with pytest.raises(B.EpdcError) as ei:
             call()
         assert ei.value.status == B.EPDC_ERR_INVALID_ARGS
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/epdc.h compiles as C99 with warnings as errors, and every
+    declared entry point can be named from C."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    names = B.header_entry_points()
+    src = tmp_path / "use_header.c"
+    src.write_text('#include "epdc.h"\n'
+                   + "typedef void (*any_fn)(void);\n"
+                   + "".join(f"any_fn p_{n} = (any_fn)&{n};\n" for n in names)
+                   + "int main(void) { return 0; }\n")
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                    "-I", os.path.join(ROOT, "include"), str(src)], check=True)
