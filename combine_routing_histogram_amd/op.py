@@ -86,6 +86,7 @@ class EpDispatchCombineOp:
             torch.cuda.current_device()
         L = B.lib()
         self._f_dispatch, self._f_combine = L.epdc_dispatch, L.epdc_combine
+        self._views = {}
         self._payload_v = self._payload_view(self._out)
         self._combined_cut = (-1, None)   # (T, (output view, weights view))
         self._side_stream = None
@@ -247,20 +248,29 @@ class EpDispatchCombineOp:
         if cfg.raw_row_bytes:
             return buf
         if cfg.quant == "none":
-            return buf.view(torch.bfloat16)
+            return self._view(buf, torch.bfloat16)
         if cfg.quant == "fp8_e4m3_b128":
-            return buf.view(torch.float8_e4m3fn)
+            return self._view(buf, torch.float8_e4m3fn)
         return buf
+
+    def _view(self, buf: torch.Tensor, dtype) -> torch.Tensor:
+        """buf viewed as dtype; the op's buffers live as long as the op, so
+        the views are made once."""
+        key = (id(buf), dtype)
+        v = self._views.get(key)
+        if v is None:
+            v = self._views[key] = buf.view(dtype)
+        return v
 
     def _scales_view(self, buf: Optional[torch.Tensor], carried: bool) -> Optional[torch.Tensor]:
         cfg = self.config
         if cfg.quant == "fp8_e4m3_b128":
-            return buf.view(torch.float32)
+            return self._view(buf, torch.float32)
         if cfg.quant == "mxfp4_b32":
             return buf
         if not carried or buf is None:
             return None
-        return buf.view(self._scales_dtype or torch.uint8)
+        return self._view(buf, self._scales_dtype or torch.uint8)
 
     def received_payload(self) -> torch.Tensor:
         return self._payload_v
