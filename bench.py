@@ -11,6 +11,9 @@ Inputs are resident in HBM before the timed region.  Prints one JSON line.
 value = tokens/s of whole steps.  roofline: the kernel with the most time,
 algorithmic bytes per launch / its mean duration from HIP events recorded on
 the launch stream around each kernel during the timed steps.
+copy_ceiling: a plain 512 MiB device copy timed in the same run, as the
+practical HBM ceiling for mixed read/write traffic, and the step's fraction
+of it.
 cold_cache: per-kernel event times of a further pass in which writing a
 512 MiB scratch buffer before every step evicts L2 and the MALL (the timed loop reuses its buffers,
 so part of each kernel's data is still cached from the step before).
@@ -187,6 +190,9 @@ def main() -> int:
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="steps of an extra per-kernel event pass in which writing a 512 MiB "
                          "scratch buffer before each step evicts L2 and the MALL (0 = skip)")
+    ap.add_argument("--copy-ceiling", type=int, default=1,
+                    help="also time a plain 512 MiB device copy as the practical HBM ceiling "
+                         "(0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the CPU-oracle baseline (0 = skip)")
     args = ap.parse_args()
@@ -315,6 +321,22 @@ def main() -> int:
         kernels[name] = {"launches": n, "avg_us": avg * 1e3, "alg_bytes": b,
                          "gbps": b / (avg * 1e-3) / 1e9 if b else None,
                          "frac": b / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS if b else None}
+    # practical ceiling: a plain 512 MiB device-to-device copy (read + write)
+    copy_gbps = None
+    if args.copy_ceiling:
+        a_buf = torch.empty(256 << 20, dtype=torch.int16, device=dev)
+        b_buf = torch.empty_like(a_buf)
+        for _ in range(3):
+            b_buf.copy_(a_buf)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(10):
+            b_buf.copy_(a_buf)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_gbps = 2 * a_buf.numel() * 2 / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+        del a_buf, b_buf
+
     cold_kernels = None
     if cold is not None:
         cold_kernels = {}
@@ -371,6 +393,9 @@ def main() -> int:
         "step_alg_bytes": step_bytes,
         "step_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_frac_of_hbm_peak": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "copy_ceiling": None if copy_gbps is None else {
+            "kernel": "512 MiB device-to-device copy (torch copy_)", "gbps": copy_gbps,
+            "step_frac_of_copy": step_bytes / (ms_step * 1e-3) / 1e9 / copy_gbps},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": dk["gbps"],
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dk["frac"],
                      "traffic": traffic},
