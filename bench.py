@@ -157,7 +157,8 @@ def cpu_baseline(w, inp, budget_s: float, gpu_payload, gpu_scales, gpu_combined,
             and np.array_equal(gpu_combined, y))
     if d["out_scales"] is not None:
         same = same and np.array_equal(gpu_scales[:n], d["out_scales"].view(np.uint8).reshape(n, -1))
-    base = {"value": w.tokens * reps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    base = {"value": w.tokens * reps / el, "unit": "tokens/s", "cores": 1,
+            "host_cores": os.cpu_count(), "kind": "oracle",
             "sample": f"{reps} whole {'rank-deduplicated ' if dedup else ''}"
                       f"dispatch+combine steps of {w.name} "
                       f"({w.tokens} tokens each), {el:.1f} s"}
