@@ -269,6 +269,23 @@ epdc_status grid_for_waves(int64_t waves, int *grid, int *block)
     return EPDC_SUCCESS;
 }
 
+// Blocks of wpb waves for `waves` one-wave items; in XCD order (xcd_item)
+// a whole number of rounds of kXcds blocks.
+int blocks_for(int64_t waves, int wpb, bool xcd_order)
+{
+    if (!xcd_order)
+        return (int)((waves + wpb - 1) / wpb);
+    const int64_t round = (int64_t)kXcds * wpb;
+    return (int)(kXcds * ((waves + round - 1) / round));
+}
+
+// Items in XCD order for a batch of at most one routing tile.  The scatter
+// of such a batch (inline routing or its replay) and the gather combine
+// after it split rows into the same 2 KiB segments, so the two waves of a
+// (token, segment) share an XCD; larger batches keep launch order (their
+// rows do not fit the L2s anyway).
+bool one_tile_xcd_order(int64_t n_pairs) { return n_pairs > 0 && n_pairs <= kRouteTile; }
+
 // Plan, grid and launch of the scatter kernel for the op's payload kind;
 // sa holds everything but the plan fields.
 epdc_status launch_scatter(epdc_op *op, hipStream_t st, ScatterArgs &sa, int mode)
@@ -288,14 +305,18 @@ epdc_status launch_scatter(epdc_op *op, hipStream_t st, ScatterArgs &sa, int mod
         // share the copies (waves <= 1024 * 64 here: at most one tile of pairs)
         sa.work_waves =
             (int)std::min<int64_t>(kRouteWaves, std::max<int64_t>(1, (waves + 255) / 256));
-        grid = (int)((waves + sa.work_waves - 1) / sa.work_waves);
+        grid = blocks_for(waves, sa.work_waves, sa.xcd_order);
         block = kRouteThreads;
     } else {
         epdc_status s = grid_for_waves(waves, &grid, &block);
         if (s != EPDC_SUCCESS)
             return s;
         sa.work_waves = block / kWave;
+        grid = blocks_for(waves, sa.work_waves, sa.xcd_order);
     }
+    // the table-scanning blocks locate their tiles from launch-order items
+    if (sa.xcd_order && mode != kRouteInline && mode != kRouteReplay)
+        return fail(EPDC_ERR_INVALID_ARGS, "XCD item order is for one-tile pair routing only");
     if (mode == kRouteConvert)  // unit rows to expert rows: bytes, whatever the payload
         return launch(op, st, EPDC_KERNEL_UNITS_TO_EXPERTS, [&] {
             if (plan.ch == 8)
@@ -394,6 +415,7 @@ epdc_status launch_combine_mode(epdc_op *op, hipStream_t st, int kernel_id, Comb
     epdc_status s = grid_for_waves(rows * ca.segs, &grid, &block);
     if (s != EPDC_SUCCESS)
         return s;
+    grid = blocks_for(rows * ca.segs, block / kWave, ca.xcd_order);
     return launch(op, st, kernel_id, [&] {
         switch (c.topk) {
         case 1: launch_combine<1, MODE>(grid, block, st, ca); break;
@@ -696,6 +718,7 @@ epdc_status dispatch_impl(epdc_op *op, void *stream, int32_t num_tokens, const v
     sa.tiles = tiles;
     sa.tile_cnt16 = ra.tile_cnt16;
     sa.tiles_pad8 = tiles_pad8;
+    sa.xcd_order = inline_route && one_tile_xcd_order(n_pairs);
     s = launch_scatter(op, st, sa,
                        dedup ? kRouteUnits
                              : (inline_route ? kRouteInline
@@ -891,7 +914,7 @@ epdc_status epdc_combine(epdc_op *op, void *stream, const void *input, const flo
     ca.weights = weights;
     ca.output = static_cast<uint8_t *>(output);
     ca.out_weights = out_weights;
-    (void)c;
+    ca.xcd_order = one_tile_xcd_order((int64_t)T * c.topk);
     const epdc_status s = launch_combine_mode<kCombinePairs>(
         op, static_cast<hipStream_t>(stream), EPDC_KERNEL_COMBINE, ca, T);
     return s == EPDC_SUCCESS ? ok() : s;
@@ -1003,6 +1026,8 @@ epdc_status epdc_dispatch_replay(epdc_op *op, void *stream, const void *input,
         sa.unit_of = op->i32(op->lay.unit_of);
         sa.unit_rows_max = T * units_per_token(c);
         mode = kRouteUnitsReplay;
+    } else {
+        sa.xcd_order = one_tile_xcd_order(sa.n_pairs);
     }
     epdc_status s = launch_scatter(op, static_cast<hipStream_t>(stream), sa, mode);
     return s == EPDC_SUCCESS ? ok() : s;

@@ -446,6 +446,7 @@ struct ScatterArgs {
     int32_t tiles;                     // routing tiles (kRouteTableScan)
     const uint16_t *tile_cnt16;        // [E][tiles_pad8] tile counts (kRouteTableScan)
     int32_t tiles_pad8;
+    int32_t xcd_order;                 // 1: (token, segment) items in XCD order (xcd_item)
 };
 
 // ---- inline routing for a single tile (num_tokens * K <= kRouteTile) ----
@@ -560,6 +561,21 @@ struct ScatterWave {
     int lane, t, base, end, slot;
 };
 
+// Work item of wave w of block b (W waves per block) when items are dealt
+// to the XCDs one at a time.  The dispatcher hands a launch's blocks to the
+// chip's eight XCDs in turn, block b to XCD b % 8, so item j runs on XCD
+// j % 8 whatever the block size.  A scatter and a combine that both number
+// (token, segment) items this way run the two waves of one item on the same
+// XCD, where the combine finds the rows the scatter just wrote in that XCD's
+// L2 instead of fetching them across the chip.  The grid is a multiple of
+// kXcds blocks; items past the end have no work.
+constexpr int kXcds = 8;
+
+__device__ inline int xcd_item(int b, int W, int w)
+{
+    return kXcds * ((b / kXcds) * W + w) + b % kXcds;
+}
+
 // Token, segment and range of this wave; false if it has no work.
 __device__ inline bool scatter_wave_range(const ScatterArgs &a, int row_vecs, ScatterWave &w,
                                           int &seg)
@@ -569,7 +585,8 @@ __device__ inline bool scatter_wave_range(const ScatterArgs &a, int row_vecs, Sc
     const int wave = threadIdx.x / kWave;
     if (wave >= a.work_waves)
         return false;
-    const int wv = blockIdx.x * a.work_waves + wave;
+    const int wv = a.xcd_order ? xcd_item(blockIdx.x, a.work_waves, wave)
+                               : blockIdx.x * a.work_waves + wave;
     if (wv >= a.num_tokens * a.segs)
         return false;
     // the grid covers the row capacity; rows past the device count have no work
@@ -1068,6 +1085,7 @@ struct CombineArgs {
     int32_t n_pairs;           // expert rows of the recorded dispatch
     int32_t num_src_tokens;    // tokens of the recorded dispatch
     int32_t in_rows_max;       // rows of the unit-row input
+    int32_t xcd_order;         // 1: (row, segment) items in XCD order (xcd_item)
 };
 
 // What a combine wave sums.
@@ -1233,7 +1251,9 @@ template <int KT, int CH = kCombineSeg, int MODE = kCombinePairs>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int wv = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int wpb = blockDim.x / kWave;
+    const int wv = a.xcd_order ? xcd_item(blockIdx.x, wpb, threadIdx.x / kWave)
+                               : blockIdx.x * wpb + threadIdx.x / kWave;
     if (wv >= a.num_tokens * a.segs)
         return;
     const int t = wv / a.segs;  // output row: a token, or a unit for kCombineUnitsIn

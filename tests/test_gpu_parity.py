@@ -408,3 +408,29 @@ def test_scatter_blocks_straddling_two_tiles():
     x = wl.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     idx = wl.draw_topk(rng, T, E, K, "zipf", 1.1)
     run_case(x, wl.softmax_weights(rng, T, K), idx, E, R)
+
+
+@pytest.mark.parametrize("T,H,K", [
+    (1024, 7168, 1),   # 7168 waves: 16 copying waves per routing block, 4-wave combine blocks
+    (100, 7168, 10),   # 700 waves: 3 per routing block
+    (73, 1000, 14),    # 73 waves, one per row: a partial round of blocks
+    (341, 4104, 3),    # 1705 waves, 5 segments with a ragged last one: 7 per block
+    (512, 2056, 2),    # 1536 waves: 6 per block
+])
+def test_one_tile_xcd_order(T, H, K):
+    """Batches of one routing tile number their (token, segment) items in XCD
+    order in the scatter, its replay and the combine; the grids are whole
+    rounds of 8 blocks, so the last round holds items past the end."""
+    log(f"xcd order T={T} H={H} K={K}")
+    rng = np.random.default_rng(T * 31 + K)
+    E, R = 64, 4
+    idx = wl.draw_topk(rng, T, E, K, "uniform")
+    x = wl.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    w = wl.softmax_weights(rng, T, K)
+    op, ref = run_case(x, w, idx, E, R)
+    x2 = wl.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    out2 = op.dispatch_replay(bf16_dev(x2), torch.from_numpy(w).to(DEV), None)[0]
+    torch.cuda.synchronize()
+    n = ref["n_valid"]
+    ref2 = oracle.dispatch(x2, w, idx, E, R)
+    np.testing.assert_array_equal(bits16(out2[:n]), ref2["out"], err_msg="replay payload")
