@@ -453,40 +453,108 @@ struct ScatterArgs {
 //
 // With at most one routing tile there is nothing to scan across blocks, so
 // the scatter launch routes by itself and dispatch is one launch.  Its blocks
-// have kRouteThreads threads: every block ranks the whole tile exactly like
-// k_route_rank (one pair per thread) and scans the histogram into expert
-// offsets, all in LDS, then its first work_waves waves copy their (token,
-// segment) pieces with slot = expert_off[e] + rank (fewer copying waves per
-// block spread the copies over more CUs).  Block 0 publishes expert_off /
-// rank_off / recv_count and raises the error flag.
+// have kRouteThreads threads: every block ranks the whole tile (one pair per
+// thread, the same match-any ranks as k_route_rank) and scans the histogram
+// into expert offsets, all in LDS, then its first work_waves waves copy their
+// (token, segment) pieces (fewer copying waves per block spread the copies
+// over more CUs).  Block 0 publishes expert_off / rank_off / recv_count and
+// raises the error flag.  Two block barriers in all: each wave clears its own
+// row of counts (a wave's LDS operations complete in order), and the copying
+// waves assemble each pair's slot from the LDS tables instead of waiting for
+// a table of slots.
 
 struct InlineRouteLds {
-    int32_t wave_cnt[kRouteWaves * kMaxExperts];
-    int32_t eoff[kMaxExperts + 1];
-    int32_t slot[kRouteTile];
-    int32_t wave_tot[kRouteWaves + 1];
+    int32_t wave_cnt[kRouteWaves * kMaxExperts];  // [wave][e]: count, then prefix over waves
+    int32_t ebase[kMaxExperts];                   // exclusive scan inside e's 64-expert group
+    int32_t grp_tot[kMaxExperts / kWave];         // total of each 64-expert group
+    int32_t e_of[kRouteTile];                     // expert of each pair, -1 for none
+    int32_t rank_w[kRouteTile];                   // rank among the same expert in its wave
 };
+
+// First slot of expert e (e == E: the number of valid pairs).
+__device__ inline int inline_expert_off(const InlineRouteLds &l, int E, int e)
+{
+    int s = e < E ? l.ebase[e] : 0;
+    const int groups = e < E ? e / kWave : (E + kWave - 1) / kWave;
+    for (int g = 0; g < groups; ++g)
+        s += l.grp_tot[g];
+    return s;
+}
 
 __device__ inline void inline_route(const ScatterArgs &a, InlineRouteLds &l)
 {
     const int tid = threadIdx.x;
-    const bool first = blockIdx.x == 0;
-    const TileRank r = rank_tile(a.indices, a.n_pairs, a.num_experts, a.key_bits, a.topk, 0, tid,
-                                 l.wave_cnt, a.ctrl, first);
-    write_offsets(a.num_experts, a.num_ranks, r.col_total, l.eoff, l.wave_tot, a.expert_off,
-                  a.rank_off, a.recv_count, first);
-    l.slot[tid] = r.e >= 0 ? l.eoff[r.e] + r.rank : -1;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int E = a.num_experts;
+    int e = -1;
+    if (tid < a.n_pairs) {
+        const int v = a.indices[tid];
+        if (v >= 0 && v < E)
+            e = v;
+        else if (blockIdx.x == 0)
+            atomicOr(&a.ctrl[kCtrlError], 1u);
+    }
+    for (int i = lane; i < E; i += kWave)
+        l.wave_cnt[wave * E + i] = 0;
+    const bool valid = e >= 0;
+    uint64_t match = __ballot(valid);  // match-any over the expert id bits
+    for (int bit = 0; bit < a.key_bits; ++bit) {
+        const bool one = (e >> bit) & 1;
+        const uint64_t ones = __ballot(one);
+        match &= one ? ones : ~ones;
+    }
+    const int rank_in_wave = lanes_below(match);
+    if (valid && rank_in_wave == 0)
+        l.wave_cnt[wave * E + e] = __popcll(match);
+    l.e_of[tid] = e;
+    l.rank_w[tid] = rank_in_wave;
     __syncthreads();
+    if (wave * kWave < E) {  // whole waves, one expert per thread
+        int total = 0;
+        if (tid < E) {
+            int c[kRouteWaves];
+#pragma unroll
+            for (int w = 0; w < kRouteWaves; ++w)
+                c[w] = l.wave_cnt[w * E + tid];
+#pragma unroll
+            for (int w = 0; w < kRouteWaves; ++w) {
+                l.wave_cnt[w * E + tid] = total;
+                total += c[w];
+            }
+        }
+        const int incl = wave_inclusive_sum(total, lane);
+        if (tid < E)
+            l.ebase[tid] = incl - total;
+        if (lane == kWave - 1)
+            l.grp_tot[wave] = incl;
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {
+        const int R = a.num_ranks;
+        const int per_rank = E / R;
+        if (tid <= E)
+            a.expert_off[tid] = inline_expert_off(l, E, tid);
+        if (tid <= R)
+            a.rank_off[tid] = inline_expert_off(l, E, tid * per_rank);
+        if (tid < R)
+            a.recv_count[tid] = inline_expert_off(l, E, (tid + 1) * per_rank) -
+                                inline_expert_off(l, E, tid * per_rank);
+    }
 }
 
-// Slot of this lane's pair (lanes < K) from the block's slot table.
+// Slot of this lane's pair (lanes < K): the expert's first slot, plus the
+// pairs of that expert in lower waves, plus those in lower lanes of its wave.
 __device__ inline int pair_slot_inline(const ScatterArgs &a, const InlineRouteLds &l, int t,
                                        int lane, bool record)
 {
     int s = -1;
     if (lane < a.topk) {
         const int p = t * a.topk + lane;
-        s = l.slot[p];
+        const int e = l.e_of[p];
+        if (e >= 0)
+            s = inline_expert_off(l, a.num_experts, e) +
+                l.wave_cnt[(p / kWave) * a.num_experts + e] + l.rank_w[p];
         if (record) {
             if (s >= 0)
                 a.src_pos[s] = p;
