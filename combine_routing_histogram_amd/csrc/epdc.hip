@@ -286,6 +286,11 @@ int blocks_for(int64_t waves, int wpb, bool xcd_order)
 // rows do not fit the L2s anyway).
 bool one_tile_xcd_order(int64_t n_pairs) { return n_pairs > 0 && n_pairs <= kRouteTile; }
 
+// Rows a scatter writes that fit the eight XCDs' 4 MB L2s together are
+// written with ordinary stores, which leave them there for the kernel that
+// reads them next; larger batches use device-scope stores (row_rsrc).
+constexpr int64_t kL2ResidentBytes = int64_t(32) << 20;
+
 // Plan, grid and launch of the scatter kernel for the op's payload kind;
 // sa holds everything but the plan fields.
 epdc_status launch_scatter(epdc_op *op, hipStream_t st, ScatterArgs &sa, int mode)
@@ -298,6 +303,15 @@ epdc_status launch_scatter(epdc_op *op, hipStream_t st, ScatterArgs &sa, int mod
     const ScatterPlan plan = plan_scatter(quant, num_tokens, in_vecs, inline_route);
     sa.segs = plan.segs;
     sa.seg_vecs = plan.seg_vecs;
+    {
+        size_t payload, scales;
+        row_bytes_for(c, &payload, &scales);
+        if (mode == kRouteConvert)
+            payload = (size_t)sa.in_row_vecs * 16;
+        const bool unit_rows = mode == kRouteUnits || mode == kRouteUnitsReplay;
+        const int64_t rows = unit_rows ? sa.unit_rows_max : sa.n_pairs;
+        sa.cached_stores = rows * (int64_t)payload <= kL2ResidentBytes;
+    }
     int grid, block;
     const int64_t waves = (int64_t)num_tokens * sa.segs;
     if (inline_route) {
