@@ -969,6 +969,7 @@ epdc_status epdc_combine_scatter(epdc_op *op, void *stream, const void *input,
     pa.output = static_cast<uint8_t *>(output);
     pa.out_weights = out_weights;
     pa.num_tokens = T;
+    pa.cached_stores = (int64_t)pa.n_pairs * c.hidden * 4 <= kL2ResidentBytes;
     hipStream_t st = static_cast<hipStream_t>(stream);
     int grid, block;
     epdc_status s = grid_for_waves((int64_t)pa.rows * pa.segs, &grid, &block);

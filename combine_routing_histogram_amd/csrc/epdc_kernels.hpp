@@ -1447,8 +1447,18 @@ struct PushArgs {
     uint8_t *output;            // [T, H] bf16
     float *out_weights;         // [T, K] or NULL
     int32_t num_tokens;
+    int32_t cached_stores;      // 1: ordinary staging stores that stay in the L2 (small batches)
 };
 
+// Both kernels work on 4-element pieces (8 bytes of bf16, 16 bytes of fp32),
+// lane l on pieces base + l + 64 i, so every staging load and store
+// instruction covers 1 KiB of one row.  With 16-byte bf16 vectors per lane
+// each lane wrote two fp32 vectors 32 bytes apart and read them back the
+// same way; contiguous pieces took the headline push + reduce from 454 to
+// 450 us.  The push then writes a large staging buffer with device-scope
+// stores like the scatter (row_rsrc; 446 us) and one that fits the L2s with
+// ordinary stores (the decode-shaped step took 26.7 us with them against
+// 28.3 us with device scope).
 template <int CH>
 __global__ __launch_bounds__(256) void k_combine_push(PushArgs a)
 {
@@ -1465,50 +1475,51 @@ __global__ __launch_bounds__(256) void k_combine_push(PushArgs a)
         return;
     const int K = a.topk;
     const float w = a.weights ? a.weights[(size_t)s * K + p % K] : 1.0f;
-    const int V = a.row_vecs;
-    const u32x4 *row = reinterpret_cast<const u32x4 *>(a.input) + (size_t)s * V;
-    f32x4 *dst = reinterpret_cast<f32x4 *>(a.staging) + (size_t)p * V * 2;
-    u32x4 v[CH];
+    constexpr int PC = 2 * CH;        // pieces per lane per segment
+    const int P = 2 * a.row_vecs;     // pieces per row
+    const int base = sg * kWave * PC;
+    const u32x2 *row = reinterpret_cast<const u32x2 *>(a.input) + (size_t)s * P;
+    const __amdgpu_buffer_rsrc_t dst =
+        row_rsrc(reinterpret_cast<uint8_t *>(a.staging), (size_t)P * 16, p);
+    u32x2 v[PC];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        const int j = sg * kWave * CH + lane + kWave * i;
-        if (j < V)
-            v[i] = __builtin_nontemporal_load(row + j);
+    for (int i = 0; i < PC; ++i) {
+        const int h = base + lane + kWave * i;
+        if (h < P)
+            v[i] = __builtin_nontemporal_load(row + h);
     }
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        const int j = sg * kWave * CH + lane + kWave * i;
-        if (j < V) {
+    for (int i = 0; i < PC; ++i) {
+        const int h = base + lane + kWave * i;
+        if (h < P) {
 #pragma clang fp contract(off)
-            dst[2 * j] = f32x4{w * bf16_lo(v[i].x), w * bf16_hi(v[i].x), w * bf16_lo(v[i].y),
-                               w * bf16_hi(v[i].y)};
-            dst[2 * j + 1] = f32x4{w * bf16_lo(v[i].z), w * bf16_hi(v[i].z),
-                                   w * bf16_lo(v[i].w), w * bf16_hi(v[i].w)};
+            const f32x4 prod = {w * bf16_lo(v[i].x), w * bf16_hi(v[i].x), w * bf16_lo(v[i].y),
+                                w * bf16_hi(v[i].y)};
+            if (a.cached_stores)
+                reinterpret_cast<f32x4 *>(a.staging)[(size_t)p * P + h] = prod;
+            else
+                store_row16(dst, h * 16, __builtin_bit_cast(u32x4, prod));
         }
     }
 }
 
-// Sum of NT staging rows (lane k < NT holds the k-th pair), double buffered.
-template <int NT, int CH>
-__device__ inline void sum_staged(const f32x4 *st, int V, int base, int lane, int my_pair,
-                                  float (&acc)[CH][8])
+// Sum of NT staging rows (lane k < NT holds the k-th pair), double buffered;
+// PC pieces per lane starting at piece `base`.
+template <int NT, int PC>
+__device__ inline void sum_staged(const f32x4 *st, int P, int base, int lane, int my_pair,
+                                  float (&acc)[PC][4])
 {
     int pr[NT];
 #pragma unroll
     for (int k = 0; k < NT; ++k)
         pr[k] = read_lane(my_pair, k);
-    f32x4 buf[2][CH][2];
-    auto load = [&](int p, f32x4 (&d)[CH][2]) {
-        const f32x4 *r = st + (size_t)p * V * 2;
+    f32x4 buf[2][PC];
+    auto load = [&](int p, f32x4 (&d)[PC]) {
+        const f32x4 *r = st + (size_t)p * P;
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int j = base + lane + kWave * i;
-            if (j < V) {
-                d[i][0] = __builtin_nontemporal_load(r + 2 * j);
-                d[i][1] = __builtin_nontemporal_load(r + 2 * j + 1);
-            } else {
-                d[i][0] = d[i][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            }
+        for (int i = 0; i < PC; ++i) {
+            const int h = base + lane + kWave * i;
+            d[i] = h < P ? __builtin_nontemporal_load(r + h) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
     };
     load(pr[0], buf[0]);
@@ -1517,29 +1528,25 @@ __device__ inline void sum_staged(const f32x4 *st, int V, int base, int lane, in
         if (k + 1 < NT)
             load(pr[k + 1], buf[(k + 1) & 1]);
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
+        for (int i = 0; i < PC; ++i) {
 #pragma clang fp contract(off)
-            acc[i][0] = acc[i][0] + buf[k & 1][i][0].x;
-            acc[i][1] = acc[i][1] + buf[k & 1][i][0].y;
-            acc[i][2] = acc[i][2] + buf[k & 1][i][0].z;
-            acc[i][3] = acc[i][3] + buf[k & 1][i][0].w;
-            acc[i][4] = acc[i][4] + buf[k & 1][i][1].x;
-            acc[i][5] = acc[i][5] + buf[k & 1][i][1].y;
-            acc[i][6] = acc[i][6] + buf[k & 1][i][1].z;
-            acc[i][7] = acc[i][7] + buf[k & 1][i][1].w;
+            acc[i][0] = acc[i][0] + buf[k & 1][i].x;
+            acc[i][1] = acc[i][1] + buf[k & 1][i].y;
+            acc[i][2] = acc[i][2] + buf[k & 1][i].z;
+            acc[i][3] = acc[i][3] + buf[k & 1][i].w;
         }
     }
 }
 
-template <int KT, int CH, int NT = 1>
-__device__ inline void sum_staged_n(int n, const f32x4 *st, int V, int base, int lane,
-                                    int my_pair, float (&acc)[CH][8])
+template <int KT, int PC, int NT = 1>
+__device__ inline void sum_staged_n(int n, const f32x4 *st, int P, int base, int lane,
+                                    int my_pair, float (&acc)[PC][4])
 {
     if constexpr (NT <= KT) {
         if (n == NT)
-            sum_staged<NT, CH>(st, V, base, lane, my_pair, acc);
+            sum_staged<NT, PC>(st, P, base, lane, my_pair, acc);
         else
-            sum_staged_n<KT, CH, NT + 1>(n, st, V, base, lane, my_pair, acc);
+            sum_staged_n<KT, PC, NT + 1>(n, st, P, base, lane, my_pair, acc);
     }
 }
 
@@ -1573,30 +1580,30 @@ __global__ __launch_bounds__(256) void k_combine_reduce(PushArgs a)
         if (read_lane(r, j) == lane)
             cp = pj;
     }
-    const int V = a.row_vecs;
-    const int base = sg * kWave * CH;
-    float acc[CH][8];
+    constexpr int PC = 2 * CH;     // pieces per lane per segment
+    const int P = 2 * a.row_vecs;  // pieces per row
+    const int base = sg * kWave * PC;
+    float acc[PC][4];
 #pragma unroll
-    for (int i = 0; i < CH; ++i)
+    for (int i = 0; i < PC; ++i)
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < 4; ++q)
             acc[i][q] = 0.0f;
     const f32x4 *st = reinterpret_cast<const f32x4 *>(a.staging);
     if constexpr (KT > 0) {
-        sum_staged_n<KT, CH>(n, st, V, base, lane, cp, acc);
+        sum_staged_n<KT, PC>(n, st, P, base, lane, cp, acc);
     } else {
         for (int k = 0; k < n; ++k)  // one row at a time
-            sum_staged<1, CH>(st, V, base, lane, read_lane(cp, k), acc);
+            sum_staged<1, PC>(st, P, base, lane, read_lane(cp, k), acc);
     }
-    u32x4 *out = reinterpret_cast<u32x4 *>(a.output) + (size_t)t * V;
+    u32x2 *out = reinterpret_cast<u32x2 *>(a.output) + (size_t)t * P;
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        const int j = base + lane + kWave * i;
-        if (j < V)
+    for (int i = 0; i < PC; ++i) {
+        const int h = base + lane + kWave * i;
+        if (h < P)
             __builtin_nontemporal_store(
-                u32x4{pack_bf16_rne(acc[i][0], acc[i][1]), pack_bf16_rne(acc[i][2], acc[i][3]),
-                      pack_bf16_rne(acc[i][4], acc[i][5]), pack_bf16_rne(acc[i][6], acc[i][7])},
-                out + j);
+                u32x2{pack_bf16_rne(acc[i][0], acc[i][1]), pack_bf16_rne(acc[i][2], acc[i][3])},
+                out + h);
     }
 }
 
