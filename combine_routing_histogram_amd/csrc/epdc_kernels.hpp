@@ -942,7 +942,9 @@ __device__ inline void route_wave(const ScatterArgs &a, bool has_work, int seg, 
 // the L2s (cached_stores; at the decode shape the combine took 3.9 -> 5.6 us
 // after device-scope stores) keeps ordinary stores, and so do the MXFP4
 // kernel's 4-byte stores (77.5-80.1 -> 81.1 us).
-constexpr int kBufferDword3 = 0x00020000;  // raw (untyped) buffer access on gfx9-family parts
+// Fourth descriptor word: DATA_FORMAT = 32 bits (bits 15-18 = 4); untyped
+// MUBUF accesses need a nonzero data format on gfx9-family parts.
+constexpr int kBufferDword3 = 0x00020000;
 constexpr int kStoreDeviceScope = 16;      // cache policy: sc1
 
 __device__ inline __amdgpu_buffer_rsrc_t row_rsrc(uint8_t *base, size_t row_bytes, int row)
