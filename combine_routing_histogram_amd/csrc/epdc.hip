@@ -39,6 +39,10 @@ epdc_status ok()
     return EPDC_SUCCESS;
 }
 
+// Largest row (elements): rows are addressed with 32-bit byte offsets, and an
+// fp32 staging row is 4H bytes.
+constexpr int kMaxHidden = 1 << 24;
+
 constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -65,6 +69,8 @@ epdc_status check_config(const epdc_config *c)
         return fail(EPDC_ERR_INVALID_ARGS, "max_tokens must be >= 0");
     if (c->hidden <= 0 || c->hidden % 8 != 0)
         return fail(EPDC_ERR_INVALID_ARGS, "hidden must be a positive multiple of 8");
+    if (c->hidden > kMaxHidden)
+        return fail(EPDC_ERR_INVALID_ARGS, "hidden must be <= 2^24");
     if (c->topk < 1 || c->topk > kMaxTopk)
         return fail(EPDC_ERR_INVALID_ARGS, "topk must be in [1, %d]", kMaxTopk);
     if (c->num_experts < 1 || c->num_experts > kMaxExperts)
@@ -97,8 +103,10 @@ epdc_status check_config(const epdc_config *c)
         if (c->scale_row_bytes != 0)
             return fail(EPDC_ERR_INVALID_ARGS, "scale_row_bytes must be 0 when dispatch quantizes");
     }
-    if (c->input_kind == EPDC_IN_RAW && (c->raw_row_bytes <= 0 || c->raw_row_bytes % 16 != 0))
-        return fail(EPDC_ERR_INVALID_ARGS, "raw_row_bytes must be a positive multiple of 16");
+    if (c->input_kind == EPDC_IN_RAW && (c->raw_row_bytes <= 0 || c->raw_row_bytes % 16 != 0 ||
+                                         c->raw_row_bytes > 2 * kMaxHidden))
+        return fail(EPDC_ERR_INVALID_ARGS,
+                    "raw_row_bytes must be a positive multiple of 16, at most 2^25");
     return EPDC_SUCCESS;
 }
 

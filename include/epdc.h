@@ -85,14 +85,16 @@ typedef enum epdc_quant {
 /* Fixed at creation. */
 typedef struct epdc_config {
     int32_t max_tokens;      /* T_max >= 0: largest num_tokens of a dispatch */
-    int32_t hidden;          /* H > 0, multiple of 8 (bf16 rows of 16-byte
-                                vectors); multiple of 128 for FP8, 32 for MXFP4 */
+    int32_t hidden;          /* H in (0, 2^24], multiple of 8 (bf16 rows of
+                                16-byte vectors); multiple of 128 for FP8, 32
+                                for MXFP4 */
     int32_t topk;            /* K in [1, 16] */
     int32_t num_experts;     /* E in [1, 512] */
     int32_t num_ranks;       /* R >= 1 with E % R == 0 */
     int32_t input_kind;      /* epdc_input_kind */
     int32_t quant;           /* epdc_quant; != NONE requires EPDC_IN_BF16 */
-    int32_t raw_row_bytes;   /* EPDC_IN_RAW: bytes per row, > 0, multiple of 16 */
+    int32_t raw_row_bytes;   /* EPDC_IN_RAW: bytes per row, in (0, 2^25], multiple
+                                of 16 */
     int32_t scale_row_bytes; /* bytes per carried scale row, multiple of 4,
                                 0 = dispatch carries no scales; must be 0 when
                                 quant != NONE (scales are then produced) */

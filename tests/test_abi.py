@@ -80,6 +80,8 @@ def test_raw_carry_row_bytes(lib):
     (dict(scale_row_bytes=6), "scale_row_bytes"),
     (dict(quant=1, scale_row_bytes=8), "scale_row_bytes"),
     (dict(max_tokens=1 << 28, topk=8), "2^30"),
+    (dict(hidden=(1 << 24) + 8), "2^24"),
+    (dict(input_kind=1, raw_row_bytes=(1 << 25) + 16), "2^25"),
 ])
 def test_invalid_configs_rejected(lib, kw, msg):
     args = dict(max_tokens=128, hidden=256, topk=2, num_experts=8, num_ranks=2)
