@@ -299,16 +299,45 @@ bool one_tile_xcd_order(int64_t n_pairs) { return n_pairs > 0 && n_pairs <= kRou
 // reads them next; larger batches use device-scope stores (row_rsrc).
 constexpr int64_t kL2ResidentBytes = int64_t(32) << 20;
 
+// Segment width of the XCD-local layout of a small rank-deduplicated bf16
+// batch, or 0.  Its four kernels number their rows differently (token, unit,
+// expert row), so XCD order alone cannot pair a writer wave with its reader.
+// With a multiple of 8 segments per row it does not need to: item
+// row * segs + s runs on XCD s mod 8 in every kernel, so each kernel of the
+// chain finds the rows segment s of the previous one wrote in its own L2.
+// Rows need at least 512 vectors (hidden >= 4096) so that a segment keeps
+// at least 64 vectors, one per lane.
+int dedup_local_seg_vecs(const epdc_config &c, int64_t tokens)
+{
+    if (c.quant != EPDC_QUANT_NONE || c.input_kind != EPDC_IN_BF16)
+        return 0;
+    const int V = c.hidden / 8;
+    if (V < kXcds * kWave || tokens * c.topk * 2 * (int64_t)c.hidden > kL2ResidentBytes)
+        return 0;
+    const int per_round = kXcds * kCombineSegVecs;
+    const int segs = kXcds * ((V + per_round - 1) / per_round);
+    return (V + segs - 1) / segs;
+}
+
 // Plan, grid and launch of the scatter kernel for the op's payload kind;
 // sa holds everything but the plan fields.
-epdc_status launch_scatter(epdc_op *op, hipStream_t st, ScatterArgs &sa, int mode)
+// local_seg_vecs > 0: the XCD-local layout (dedup_local_seg_vecs), rows in
+// segments of that many vectors, items in XCD order.
+epdc_status launch_scatter(epdc_op *op, hipStream_t st, ScatterArgs &sa, int mode,
+                           int local_seg_vecs = 0)
 {
     const epdc_config &c = op->cfg;
     const int num_tokens = sa.num_tokens;
     const bool inline_route = mode == kRouteInline;
     const int quant = mode == kRouteConvert ? (int)EPDC_QUANT_NONE : c.quant;
     const int in_vecs = quant == EPDC_QUANT_NONE ? sa.in_row_vecs : c.hidden / 8;
-    const ScatterPlan plan = plan_scatter(quant, num_tokens, in_vecs, inline_route);
+    ScatterPlan plan = plan_scatter(quant, num_tokens, in_vecs, inline_route);
+    if (local_seg_vecs > 0) {
+        plan.ch = 2;  // one pass of up to 128 vectors per segment
+        plan.seg_vecs = local_seg_vecs;
+        plan.segs = (in_vecs + local_seg_vecs - 1) / local_seg_vecs;
+        sa.xcd_order = 1;
+    }
     sa.segs = plan.segs;
     sa.seg_vecs = plan.seg_vecs;
     {
@@ -337,8 +366,8 @@ epdc_status launch_scatter(epdc_op *op, hipStream_t st, ScatterArgs &sa, int mod
         grid = blocks_for(waves, sa.work_waves, sa.xcd_order);
     }
     // the table-scanning blocks locate their tiles from launch-order items
-    if (sa.xcd_order && mode != kRouteInline && mode != kRouteReplay)
-        return fail(EPDC_ERR_INVALID_ARGS, "XCD item order is for one-tile pair routing only");
+    if (sa.xcd_order && mode == kRouteTableScan)
+        return fail(EPDC_ERR_INVALID_ARGS, "XCD item order cannot scan the tile table");
     if (mode == kRouteConvert)  // unit rows to expert rows: bytes, whatever the payload
         return launch(op, st, EPDC_KERNEL_UNITS_TO_EXPERTS, [&] {
             if (plan.ch == 8)
@@ -423,15 +452,22 @@ void launch_combine(int grid, int block, hipStream_t st, const CombineArgs &a)
     k_combine<KT, kCombineSeg, MODE><<<grid, block, 0, st>>>(a);
 }
 
-// One wave per (row, 2 KiB segment) over `rows` output rows.
+// One wave per (row, 2 KiB segment) over `rows` output rows; with
+// local_seg_vecs > 0 the XCD-local layout (dedup_local_seg_vecs).
 template <int MODE>
 epdc_status launch_combine_mode(epdc_op *op, hipStream_t st, int kernel_id, CombineArgs &ca,
-                                int64_t rows)
+                                int64_t rows, int local_seg_vecs = 0)
 {
     const epdc_config &c = op->cfg;
     ca.topk = c.topk;
     ca.row_vecs = c.hidden / 8;
-    ca.segs = (ca.row_vecs + kCombineSegVecs - 1) / kCombineSegVecs;
+    ca.seg_vecs = kCombineSegVecs;
+    if (local_seg_vecs > 0) {
+        ca.seg_vecs = local_seg_vecs;
+        ca.xcd_order = 1;
+        ca.cached_stores = 1;
+    }
+    ca.segs = (ca.row_vecs + ca.seg_vecs - 1) / ca.seg_vecs;
     ca.num_tokens = (int32_t)rows;
     int grid, block;
     epdc_status s = grid_for_waves(rows * ca.segs, &grid, &block);
@@ -744,7 +780,8 @@ epdc_status dispatch_impl(epdc_op *op, void *stream, int32_t num_tokens, const v
     s = launch_scatter(op, st, sa,
                        dedup ? kRouteUnits
                              : (inline_route ? kRouteInline
-                                             : (fused_scan ? kRouteTableScan : kRouteTable)));
+                                             : (fused_scan ? kRouteTableScan : kRouteTable)),
+                       dedup ? dedup_local_seg_vecs(c, num_tokens) : 0);
     if (s != EPDC_SUCCESS)
         return s;
     op->routed = true;
@@ -846,7 +883,8 @@ epdc_status epdc_units_to_experts(epdc_op *op, void *stream, const void *input,
     sa.num_src_tokens = T;
     sa.num_ranks = c.num_ranks;
     sa.ctrl = op->ctrl();
-    const epdc_status s = launch_scatter(op, static_cast<hipStream_t>(stream), sa, kRouteConvert);
+    const epdc_status s = launch_scatter(op, static_cast<hipStream_t>(stream), sa, kRouteConvert,
+                                         dedup_local_seg_vecs(c, T));
     return s == EPDC_SUCCESS ? ok() : s;
 }
 
@@ -878,7 +916,7 @@ epdc_status epdc_experts_to_units(epdc_op *op, void *stream, const void *input,
     ca.num_src_tokens = T;
     const epdc_status s = launch_combine_mode<kCombineUnitsIn>(
         op, static_cast<hipStream_t>(stream), EPDC_KERNEL_EXPERTS_TO_UNITS, ca,
-        (int64_t)T * units_per_token(c));
+        (int64_t)T * units_per_token(c), dedup_local_seg_vecs(c, T));
     return s == EPDC_SUCCESS ? ok() : s;
 }
 
@@ -907,7 +945,8 @@ epdc_status epdc_combine_units(epdc_op *op, void *stream, const void *input,
     ca.unit_of = op->i32(op->lay.unit_of);
     ca.in_rows_max = T * units_per_token(c);
     const epdc_status s = launch_combine_mode<kCombineUnitsOut>(
-        op, static_cast<hipStream_t>(stream), EPDC_KERNEL_COMBINE_UNITS, ca, T);
+        op, static_cast<hipStream_t>(stream), EPDC_KERNEL_COMBINE_UNITS, ca, T,
+        dedup_local_seg_vecs(c, T));
     return s == EPDC_SUCCESS ? ok() : s;
 }
 
@@ -1045,14 +1084,17 @@ epdc_status epdc_dispatch_replay(epdc_op *op, void *stream, const void *input,
     sa.scale_words = c.scale_row_bytes / 4;
     sa.ctrl = op->ctrl();
     int mode = kRouteReplay;
+    int local_seg_vecs = 0;
     if (op->units_routed) {  // replay the unit rows of a rank-deduplicated dispatch
         sa.unit_of = op->i32(op->lay.unit_of);
         sa.unit_rows_max = T * units_per_token(c);
         mode = kRouteUnitsReplay;
+        local_seg_vecs = dedup_local_seg_vecs(c, T);
     } else {
         sa.xcd_order = one_tile_xcd_order(sa.n_pairs);
     }
-    epdc_status s = launch_scatter(op, static_cast<hipStream_t>(stream), sa, mode);
+    epdc_status s =
+        launch_scatter(op, static_cast<hipStream_t>(stream), sa, mode, local_seg_vecs);
     return s == EPDC_SUCCESS ? ok() : s;
 }
 

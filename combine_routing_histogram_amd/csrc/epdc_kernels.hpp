@@ -1181,7 +1181,7 @@ struct CombineArgs {
     int32_t num_tokens;
     int32_t topk;
     int32_t row_vecs;        // 16-byte vectors per bf16 row (H/8)
-    int32_t segs;            // ceil(row_vecs / kCombineSegVecs)
+    int32_t segs;            // ceil(row_vecs / seg_vecs)
     const int32_t *slot_of;  // [T*K]
     const uint8_t *input;    // [rows, H] bf16
     const float *weights;    // [rows, K] or NULL
@@ -1195,6 +1195,8 @@ struct CombineArgs {
     int32_t num_src_tokens;    // tokens of the recorded dispatch
     int32_t in_rows_max;       // rows of the unit-row input
     int32_t xcd_order;         // 1: (row, segment) items in XCD order (xcd_item)
+    int32_t seg_vecs;          // vectors per row segment (<= kWave * CH)
+    int32_t cached_stores;     // 1: ordinary output stores that stay in the L2
 };
 
 // What a combine wave sums.
@@ -1306,16 +1308,16 @@ __device__ inline int combine_slots(const CombineArgs &a, int row, int sg, int l
     }
 }
 
-// CH vectors per lane of row s's segment starting at vector `base`.
+// CH vectors per lane of row s's segment [base, end) (rows of V vectors).
 template <int CH>
-__device__ inline void load_segment(const u32x4 *in, int s, int V, int base, int lane,
+__device__ inline void load_segment(const u32x4 *in, int s, int V, int base, int end, int lane,
                                     u32x4 *dst)
 {
     const u32x4 *row = in + (size_t)s * V;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
         const int j = base + lane + kWave * i;
-        dst[i] = j < V ? __builtin_nontemporal_load(row + j) : u32x4{0u, 0u, 0u, 0u};
+        dst[i] = j < end ? __builtin_nontemporal_load(row + j) : u32x4{0u, 0u, 0u, 0u};
     }
 }
 
@@ -1323,7 +1325,7 @@ __device__ inline void load_segment(const u32x4 *in, int s, int V, int base, int
 // segments requested at once.  NT is a compile-time count so no load sits
 // behind a branch and the wait counters stay exact.
 template <int NT, int CH>
-__device__ inline void sum_rows(const u32x4 *in, int V, int base, int lane, int my_slot,
+__device__ inline void sum_rows(const u32x4 *in, int V, int base, int end, int lane, int my_slot,
                                 float my_w, float (&acc)[CH][8])
 {
     // the rows are requested before the weights are read, so the rows' loads
@@ -1331,7 +1333,7 @@ __device__ inline void sum_rows(const u32x4 *in, int V, int base, int lane, int 
     u32x4 buf[NT][CH];
 #pragma unroll
     for (int k = 0; k < NT; ++k)
-        load_segment<CH>(in, read_lane(my_slot, k), V, base, lane, buf[k]);
+        load_segment<CH>(in, read_lane(my_slot, k), V, base, end, lane, buf[k]);
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
         const float w = read_lane_f(my_w, k);
@@ -1343,19 +1345,20 @@ __device__ inline void sum_rows(const u32x4 *in, int V, int base, int lane, int 
 
 // sum_rows for the wave-uniform count n in [1, KT] (nothing for n == 0).
 template <int KT, int CH, int NT = 1>
-__device__ inline void sum_rows_n(int n, const u32x4 *in, int V, int base, int lane, int my_slot,
-                                  float my_w, float (&acc)[CH][8])
+__device__ inline void sum_rows_n(int n, const u32x4 *in, int V, int base, int end, int lane,
+                                  int my_slot, float my_w, float (&acc)[CH][8])
 {
     if constexpr (NT <= KT) {
         if (n == NT)
-            sum_rows<NT, CH>(in, V, base, lane, my_slot, my_w, acc);
+            sum_rows<NT, CH>(in, V, base, end, lane, my_slot, my_w, acc);
         else
-            sum_rows_n<KT, CH, NT + 1>(n, in, V, base, lane, my_slot, my_w, acc);
+            sum_rows_n<KT, CH, NT + 1>(n, in, V, base, end, lane, my_slot, my_w, acc);
     }
 }
 
 // KT = K known at compile time (double-buffered), or 0: runtime K <= kMaxTopk.
-// CH 16-byte vectors per lane per segment; segments are 64*CH vectors.
+// CH 16-byte vectors per lane per segment; segments are seg_vecs <= 64*CH
+// vectors.
 template <int KT, int CH = kCombineSeg, int MODE = kCombinePairs>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
 {
@@ -1379,7 +1382,8 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
         my_w = (MODE == kCombineUnitsOut || !a.weights) ? 1.0f
                                                         : a.weights[(size_t)my_slot * K + my_k];
     const int V = a.row_vecs;
-    const int base = sg * kWave * CH;
+    const int base = sg * a.seg_vecs;
+    const int end = min(V, base + a.seg_vecs);
     u32x4 *out = reinterpret_cast<u32x4 *>(a.output) + (size_t)t * V;
     const u32x4 *in = reinterpret_cast<const u32x4 *>(a.input);
     float acc[CH][8];
@@ -1391,11 +1395,11 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
 
     if constexpr (KT > 0) {
         // n == 0 leaves the sum at +0
-        sum_rows_n<KT, CH>(n, in, V, base, lane, my_slot, my_w, acc);
+        sum_rows_n<KT, CH>(n, in, V, base, end, lane, my_slot, my_w, acc);
     } else {
         for (int k = 0; k < n; ++k) {
             u32x4 buf[CH];
-            load_segment<CH>(in, read_lane(my_slot, k), V, base, lane, buf);
+            load_segment<CH>(in, read_lane(my_slot, k), V, base, end, lane, buf);
             const float wk = read_lane_f(my_w, k);
 #pragma unroll
             for (int i = 0; i < CH; ++i)
@@ -1409,15 +1413,23 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
     // Nontemporal output stores: ordinary stores of the output slow this
     // read-dominated kernel down by 10-13% when its input rows come from HBM
     // (measured on gfx950); they are 2-3% faster only when half the input is
-    // still in the MALL from the scatter that just wrote it.
+    // still in the MALL from the scatter that just wrote it.  Outputs that
+    // the next kernel reads from this XCD's L2 (cached_stores) take buffer
+    // stores with no policy bits: an ordinary global store in one branch and
+    // a nontemporal one in the other would be merged by the compiler into
+    // one store without the nontemporal hint.
+    const __amdgpu_buffer_rsrc_t orow = row_rsrc(a.output, (size_t)V * 16, t);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
         const int j = base + lane + kWave * i;
-        if (j < V)
-            __builtin_nontemporal_store(
-                u32x4{pack_bf16_rne(acc[i][0], acc[i][1]), pack_bf16_rne(acc[i][2], acc[i][3]),
-                      pack_bf16_rne(acc[i][4], acc[i][5]), pack_bf16_rne(acc[i][6], acc[i][7])},
-                out + j);
+        const u32x4 v = {pack_bf16_rne(acc[i][0], acc[i][1]), pack_bf16_rne(acc[i][2], acc[i][3]),
+                         pack_bf16_rne(acc[i][4], acc[i][5]), pack_bf16_rne(acc[i][6], acc[i][7])};
+        if (j < end) {
+            if (a.cached_stores)
+                __builtin_amdgcn_raw_buffer_store_b128(v, orow, j * 16, 0, 0);
+            else
+                __builtin_nontemporal_store(v, out + j);
+        }
     }
 }
 

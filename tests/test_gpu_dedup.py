@@ -226,3 +226,29 @@ def test_dedup_replay_and_states():
     op.units_to_experts()
     y, yw = op.combine_units()
     assert y.shape == (0, H) and yw.shape == (0, K)
+
+
+@pytest.mark.parametrize("T,H,K", [
+    (128, 4096, 8),    # 512 vectors per row: 8 segments of 64
+    (100, 4104, 8),    # 513 vectors: 8 segments of 65, the last one 58
+    (128, 7168, 8),    # the decode shape: 8 segments of 112
+    (60, 8200, 6),     # 1025 vectors: 16 segments of 65
+])
+def test_dedup_xcd_local_layout(T, H, K):
+    """Small bf16 batches run the four kernels of the deduplicated path in
+    segments of a multiple of 8 per row, in XCD order; ragged segment counts
+    and widths, plus the replay of the unit rows."""
+    log(f"dedup xcd-local T={T} H={H} K={K}")
+    rng = np.random.default_rng(T + H)
+    E, R = 64, 8
+    idx = wl.draw_topk(rng, T, E, K, "zipf", 1.1)
+    x = wl.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    w = wl.softmax_weights(rng, T, K)
+    op, ref = run_dedup(x, w, idx, E, R)
+    x2 = wl.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    op.dispatch_dedup(bf16_dev(x), torch.from_numpy(w).to(DEV), None, torch.from_numpy(idx).to(DEV))
+    out = op.dispatch_replay(bf16_dev(x2), torch.from_numpy(w).to(DEV))[0]
+    torch.cuda.synchronize()
+    ref2 = oracle.dispatch_dedup(x2, w, idx, E, R)
+    U = ref2["units"]
+    np.testing.assert_array_equal(u16(out[:U]), ref2["out"], err_msg="replayed unit rows")
