@@ -1197,6 +1197,10 @@ struct CombineArgs {
     int32_t xcd_order;         // 1: (row, segment) items in XCD order (xcd_item)
     int32_t seg_vecs;          // vectors per row segment (<= kWave * CH)
     int32_t cached_stores;     // 1: ordinary output stores that stay in the L2
+    // (Large batches keep nontemporal output stores in every mode: for the
+    // expert->unit conversion, whose output is 40% of its bytes, device-scope
+    // stores made the deduplicated headline step 404 -> 409 us and ordinary
+    // ones 414 us.)
 };
 
 // What a combine wave sums.
