@@ -254,7 +254,10 @@ ScatterPlan plan_scatter(int quant, int tokens, int row_vecs, bool inline_route)
     case EPDC_QUANT_FP8_E4M3_B128:  // 2 adjacent vectors per lane per pass
         return make_plan(kFp8PassVecs / kWave, row_vecs, 1 << 20);
     case EPDC_QUANT_MXFP4_B32:      // 2 vectors per lane per pass
-        return make_plan(2, row_vecs, 1 << 20);
+        // many tokens: one wave per row up to the scale stage (kMxStageBytes)
+        return tokens >= 2048 && !inline_route
+                   ? make_plan(2, row_vecs, (row_vecs + 4 * kMxStageBytes - 1) / (4 * kMxStageBytes))
+                   : make_plan(2, row_vecs, 1 << 20);
     default:
         return tokens >= 2048 && !inline_route ? make_plan(8, row_vecs, 1)
                                                : make_plan(2, row_vecs, 1 << 20);
@@ -340,6 +343,9 @@ epdc_status launch_scatter(epdc_op *op, hipStream_t st, ScatterArgs &sa, int mod
     }
     sa.segs = plan.segs;
     sa.seg_vecs = plan.seg_vecs;
+    // word-aligned scale rows and segments that fit the stage
+    sa.scale_stage = quant == EPDC_QUANT_MXFP4_B32 && c.hidden % 128 == 0 &&
+                     plan.seg_vecs <= 4 * kMxStageBytes;
     {
         size_t payload, scales;
         row_bytes_for(c, &payload, &scales);
