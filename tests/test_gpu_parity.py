@@ -434,3 +434,22 @@ def test_one_tile_xcd_order(T, H, K):
     n = ref["n_valid"]
     ref2 = oracle.dispatch(x2, w, idx, E, R)
     np.testing.assert_array_equal(bits16(out2[:n]), ref2["out"], err_msg="replay payload")
+
+
+@pytest.mark.parametrize("T,H,K", [
+    (2100, 1152, 4),   # 144 vectors per row: one wave per row, the second pass 16 vectors
+    (2048, 4224, 8),   # 528 vectors: five passes, the last one partial
+    (2300, 928, 2),    # hidden % 128 != 0: scale bytes stored one by one
+])
+def test_mxfp4_one_wave_per_row(T, H, K):
+    """Many tokens: the MXFP4 scatter runs one wave per row and stores the
+    row's scale bytes from its LDS stage as words; widths that are not a
+    multiple of 128 keep byte stores."""
+    log(f"mxfp4 rows T={T} H={H} K={K}")
+    rng = np.random.default_rng(T + H + K)
+    E, R = 64, 4
+    idx = wl.draw_topk(rng, T, E, K, "zipf", 1.3)
+    x = wl.f32_to_bf16_bits((rng.standard_normal((T, H)) *
+                             np.where(rng.random((T, H)) < 0.01, 20.0, 1.0)).astype(np.float32))
+    c_in = wl.f32_to_bf16_bits(rng.standard_normal((T * K, H)).astype(np.float32))
+    run_case(x, wl.softmax_weights(rng, T, K), idx, E, R, quant="mxfp4_b32", combine_input=c_in)
