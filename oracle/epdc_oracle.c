@@ -132,7 +132,7 @@ uint8_t oracle_e2m1_encode(double v)
     return (uint8_t)(sign | code);
 }
 
-/* ---- A1-A3: routing histogram, exclusive scan, stable slots -------------- */
+/* ---- Routing: histogram, exclusive scan, stable slots -------------------- */
 
 /*
  * indices [T*K] (row-major [T,K]).  Outputs: cnt[E], expert_off[E+1],
@@ -189,7 +189,7 @@ int oracle_route(int T, int K, int E, int R, const int32_t *indices,
     return invalid;
 }
 
-/* ---- A4 / A4': copy each token's row to the rows of its pairs ------------ */
+/* ---- Row copy (bf16 or pre-quantized bytes) to the rows of a token's pairs */
 
 /* dst[slot_of[t*K+k]] = src[t] for every valid pair; row_bytes per row. */
 void oracle_scatter_rows(int T, int K, const int32_t *slot_of,
@@ -205,7 +205,7 @@ void oracle_scatter_rows(int T, int K, const int32_t *slot_of,
         }
 }
 
-/* ---- A5: FP8 E4M3 with one fp32 scale per 128 elements ------------------ */
+/* ---- FP8 E4M3 with one fp32 scale per 128 elements ---------------------- */
 
 /* x [T,H] bf16 bits -> q [T,H] E4M3 codes, scales [T,H/128] fp32. */
 int oracle_quant_fp8(int T, int H, const uint16_t *x, uint8_t *q, float *scales)
@@ -239,7 +239,7 @@ int oracle_quant_fp8(int T, int H, const uint16_t *x, uint8_t *q, float *scales)
     return 0;
 }
 
-/* ---- A6: MXFP4, E2M1 codes two per byte, one E8M0 scale per 32 ----------- */
+/* ---- MXFP4: E2M1 codes two per byte, one E8M0 scale per 32 ---------------- */
 
 /* x [T,H] bf16 bits -> q [T,H/2] (element 2m in the low nibble of byte m),
  * scales [T,H/32] E8M0 bytes (biased exponent, bias 127). */
@@ -280,7 +280,7 @@ int oracle_quant_mxfp4(int T, int H, const uint16_t *x, uint8_t *q, uint8_t *sca
     return 0;
 }
 
-/* ---- B1: gather combine, fp32 accumulation, bf16 output ------------------ */
+/* ---- Gather combine: fp32 accumulation, bf16 output ---------------------- */
 
 /*
  * in [N_cap,H] bf16 bits in the received layout, weights [N_cap,K] fp32 in the
@@ -471,7 +471,7 @@ void oracle_units_to_experts(long n_pairs, const int32_t *slot_of, const int32_t
  * partial[u] = bf16_rne(sum over k = 0..K-1 with unit_of[t*K+k] == u of
  * w(t,k) * in[slot_of[t*K+k]]), fp32 separate multiply and add from +0.0f;
  * w(t,k) = weights[slot][k] with slot = slot_of[t*K+k], or 1 when weights is
- * NULL (the weighting of B1's combine, applied on the expert side).
+ * NULL (the weighting of the gather combine, applied on the expert side).
  */
 void oracle_experts_to_units(int U, int H, int K, const int32_t *unit_src,
                              const int32_t *unit_of, const int32_t *slot_of,

@@ -42,9 +42,14 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    # EPDC_ORACLE_LIB: a separately built copy of the oracle (the mutation
+    # tests build copies with planted mistakes and run the pins against them)
+    path = os.environ.get("EPDC_ORACLE_LIB")
+    if not path:
+        path = _LIB_PATH
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            build()
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     I = ctypes.c_int
     L = ctypes.c_long
@@ -103,7 +108,7 @@ def f32_to_bf16(v) -> np.ndarray:
     return out
 
 
-# ---- A1-A3 ------------------------------------------------------------------
+# ---- routing: histogram, exclusive scan, stable slots ------------------------
 
 def route(indices: np.ndarray, num_experts: int, num_ranks: int) -> Dict[str, np.ndarray]:
     """Histogram, exclusive scan and stable slots for int32 indices [T,K]."""
@@ -127,7 +132,7 @@ def route(indices: np.ndarray, num_experts: int, num_ranks: int) -> Dict[str, np
             "src_token_pos": src[:n_valid].copy(), "invalid": invalid, "n_valid": n_valid}
 
 
-# ---- A4 / A4' -------------------------------------------------------------------
+# ---- row copies ----------------------------------------------------------------
 
 def scatter_rows(src_rows: np.ndarray, slot_of: np.ndarray, topk: int, n_rows: int) -> np.ndarray:
     """dst[slot_of[t*K+k]] = src_rows[t]; src_rows any dtype [T, ...]."""
@@ -140,7 +145,7 @@ def scatter_rows(src_rows: np.ndarray, slot_of: np.ndarray, topk: int, n_rows: i
     return dst
 
 
-# ---- A5 / A6 ------------------------------------------------------------------
+# ---- quantization ---------------------------------------------------------------
 
 def quant_fp8(x_bf16: np.ndarray):
     """bf16 bits [T,H] -> (E4M3 codes uint8 [T,H], fp32 scales [T,H/128])."""
