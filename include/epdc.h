@@ -18,8 +18,8 @@
  * inside an expert ordered by the pair index p = t*K + k.  Virtual rank r owns
  * experts [r*E/R, (r+1)*E/R), i.e. the slots [rank_off[r], rank_off[r+1]).
  * recv_count[r] = rank_off[r+1] - rank_off[r] is produced by dispatch itself,
- * zero included (same page, "AsyncLL v2 SDMA overlap" section: the receive
- * side writes the total including zero; dispatch kernels produce the count).
+ * zero included (same page, "AsyncLL v2 SDMA overlap" section: a peer's
+ * count arrives even when it is zero, and the dispatch kernels compute it).
  *
  * Conventions for every entry point:
  *  - Pointers marked "device" are HBM addresses on the op's device; the
@@ -28,8 +28,8 @@
  *    written before the call returns.
  *  - `stream` is a hipStream_t passed as void*; NULL is the null stream.  The
  *    work is enqueued on it and the call returns without waiting; results are
- *    valid once that work completes (same page, AsyncLL section: data and
- *    counts are ready after the receive phase completes on the stream).
+ *    valid once that work completes (same page, AsyncLL section: payload
+ *    and counts may be used once the stream has finished the receive step).
  *  - Row-major layouts; no padding between rows.  Payload rows (input, out,
  *    output) start 16-byte aligned, every other array 4-byte aligned;
  *    misaligned pointers give EPDC_ERR_INVALID_ARGS.
@@ -298,8 +298,8 @@ epdc_status epdc_dispatch_replay(epdc_op *op, void *stream, const void *input,
 /*
  * Split phases for overlapping other work with dispatch and combine
  * ("Communication APIs" page, methods table: dispatch_send / dispatch_recv,
- * combine_send / combine_recv; "AsyncLL v2 SDMA overlap" section: data and
- * counts are ready once the receive phase completes on the stream).  On one
+ * combine_send / combine_recv; "AsyncLL v2 SDMA overlap" section: payload
+ * and counts may be used once the stream has finished the receive step).  On one
  * GPU the send phase is the whole operation enqueued on `stream` (typically a
  * side stream) followed by a completion marker owned by the op; the receive
  * phase makes `stream` (typically the compute stream) wait for that marker,
@@ -318,8 +318,9 @@ epdc_status epdc_combine_send(epdc_op *op, void *stream, const void *input,
 epdc_status epdc_combine_recv(epdc_op *op, void *stream);
 
 /* Device pointer to src_token_pos [T_max*K] int32 of the last dispatch: for
- * slot s < n_valid, the pair index p = t*K + k it came from ("Get source
- * positions of dispatched tokens (for verification)", methods table).
+ * slot s < n_valid, the pair index p = t*K + k it came from (the methods
+ * table's get_dispatch_src_token_pos, which reports where each received
+ * token came from, for checking a dispatch).
  * *count = num_tokens*K of that dispatch (host).  BAD_STATE if none. */
 epdc_status epdc_get_dispatch_src_token_pos(epdc_op *op, const int32_t **dev_ptr,
                                             int32_t *count);

@@ -15,9 +15,9 @@
  *    segment of one receive buffer.  Inside an expert, rows are ordered by the
  *    pair index p = t*K + k (stable by source token).
  *  - recv_count: produced by dispatch itself, zero for ranks that receive
- *    nothing ("AsyncLL v2 SDMA overlap" section of the same page: the receive
- *    copy writes the total, including zero; the dispatch kernels produce the
- *    count).
+ *    nothing ("AsyncLL v2 SDMA overlap" section of the same page: a peer's
+ *    count arrives even when it is zero, and it is computed by the dispatch
+ *    kernels rather than reset by the host).
  *  - get_dispatch_src_token_pos(): per received row, the pair index p it came
  *    from (same methods table).
  *  - combine(input, weights, indices) -> (output, weights): gather combine with
