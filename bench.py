@@ -5,7 +5,9 @@ bf16 rows with their weights/indices) followed by one combine (gather + fp32
 weighted top-k sum) of the dispatched rows (identity experts), by default on
 the DeepSeek-V3-shaped workload: 4096 tokens x hidden 7168, top-8 of 256
 experts (Zipf 1.1 routing), 8 virtual ranks.  --workload picks another one
-(the quantizing workloads combine an independent bf16 expert output).
+(the quantizing workloads, and the one whose FP8 rows were quantized before
+dispatch and are carried as bytes with their scales, combine an independent
+bf16 expert output).
 Inputs are resident in HBM before the timed region.  Prints one JSON line.
 
 value = tokens/s of whole steps.  roofline: the kernel with the most time,
@@ -35,10 +37,23 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published figure
 
 
+def row_sizes(w):
+    """(input row bytes the scatter reads per token, payload P and scale Q
+    bytes per received row).  Raw workloads read and carry their byte row and
+    its scale row unchanged."""
+    H = w.hidden
+    if w.raw_row_bytes:
+        return w.raw_row_bytes + w.scale_row_bytes, w.raw_row_bytes, w.scale_row_bytes
+    P, Q = {"none": (2 * H, 0), "fp8_e4m3_b128": (H, 4 * H // 128),
+            "mxfp4_b32": (H // 2, H // 32)}[w.quant]
+    return 2 * H, P, Q
+
+
 def alg_bytes_units(kernel: str, w, units: int) -> int:
     """Algorithmic bytes of the rank-deduplicated path's launches, for U =
     `units` unit rows (one per (token, destination rank)):
-      dispatch scatter:   read x (2H) + weights and indices (8K) per token;
+      dispatch scatter:   read x (2H; a raw row and its scales: P + Q) +
+                          weights and indices (8K) per token;
                           write U rows (P + Q + 8K carried), slot_of,
                           src_token_pos and unit_of (12K) per token, unit_src (4U)
       units_to_experts:   read U rows (P + Q + 8K) and unit_src; read unit_of
@@ -51,10 +66,9 @@ def alg_bytes_units(kernel: str, w, units: int) -> int:
     T, H, K = w.tokens, w.hidden, w.topk
     N = T * K
     U = units
-    P, Q = {"none": (2 * H, 0), "fp8_e4m3_b128": (H, 4 * H // 128),
-            "mxfp4_b32": (H // 2, H // 32)}[w.quant]
+    X, P, Q = row_sizes(w)
     if kernel.startswith("k_scatter"):
-        return T * (2 * H + 8 * K + 12 * K) + U * (P + Q + 8 * K + 4)
+        return T * (X + 8 * K + 12 * K) + U * (P + Q + 8 * K + 4)
     if kernel == "k_units_to_experts":
         return U * (P + Q + 8 * K + 4) + 8 * N + N * (P + Q + 8 * K)
     if kernel == "k_experts_to_units":
@@ -72,7 +86,8 @@ def alg_bytes(kernel: str, w) -> int:
     """Algorithmic bytes one launch of `kernel` must move for workload w.
 
     Per token (N = T*K pairs, P/Q = payload/scale bytes per received row):
-      scatter: read the row (2H) + weights and indices (8K); write K rows
+      scatter: read the row (2H; a raw row and its scales: P + Q) + weights
+               and indices (8K); write K rows
                (K*(P+Q)), each slot's weight and index rows (8K^2), slot_of
                and src_token_pos (8K)
       combine: read K rows (2KH) + slot_of and the K weights (8K); write
@@ -81,10 +96,9 @@ def alg_bytes(kernel: str, w) -> int:
                only touches the small tile table (counted as 0)
     """
     T, H, K = w.tokens, w.hidden, w.topk
-    P, Q = {"none": (2 * H, 0), "fp8_e4m3_b128": (H, 4 * H // 128),
-            "mxfp4_b32": (H // 2, H // 32)}[w.quant]
+    X, P, Q = row_sizes(w)
     if kernel.startswith("k_scatter"):
-        per = 2 * H + 8 * K + K * (P + Q) + 8 * K * K + 8 * K
+        per = X + 8 * K + K * (P + Q) + 8 * K * K + 8 * K
     elif kernel == "k_combine":
         per = 2 * K * H + 8 * K + 2 * H + 4 * K
     elif kernel == "k_combine_push":
@@ -135,12 +149,12 @@ def cpu_baseline(w, inp, budget_s: float, gpu_payload, gpu_scales, gpu_combined,
     while True:
         if not dedup:
             d = oracle.dispatch(inp["x"], inp["weights"], inp["indices"], w.experts, w.ranks,
-                                quant=w.quant)
+                                quant=w.quant, scales=inp.get("scales"))
             c_in = d["out"] if identity else inp["combine_input"]
             y, _ = oracle.combine(c_in, d["out_weights"], d["slot_of"], w.tokens, w.topk)
         else:
             d = oracle.dispatch_dedup(inp["x"], inp["weights"], inp["indices"], w.experts,
-                                      w.ranks, quant=w.quant)
+                                      w.ranks, quant=w.quant, scales=inp.get("scales"))
             n = d["n_valid"]
             e_out = oracle.units_to_experts(d["out"], d["slot_of"], d["unit_of"], n)
             e_w = oracle.units_to_experts(d["out_weights"], d["slot_of"], d["unit_of"], n)
@@ -220,22 +234,26 @@ def main() -> int:
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
     inp = wl.make_inputs(w)
-    x = to_bf16(inp["x"])
+    raw = w.raw_row_bytes > 0
+    x = torch.from_numpy(inp["x"]).to(dev) if raw else to_bf16(inp["x"])
+    sc = torch.from_numpy(inp["scales"]).to(dev) if raw else None
     idx = torch.from_numpy(inp["indices"]).to(dev)
     wts = torch.from_numpy(inp["weights"]).to(dev)
     identity = w.combine_input == "identity"
     c_in = None if identity else to_bf16(inp["combine_input"])
     op = EpDispatchCombineOp(EpDispatchCombineConfig(w.tokens, w.hidden, w.topk, w.experts,
-                                                     w.ranks, quant=w.quant), dev)
+                                                     w.ranks, quant=w.quant,
+                                                     raw_row_bytes=w.raw_row_bytes,
+                                                     scale_row_bytes=w.scale_row_bytes), dev)
 
     dedup = args.path == "dedup"
 
     def step():
         if not dedup:
-            out, out_w, _, out_idx, _ = op.dispatch(x, wts, None, idx)
+            out, out_w, _, out_idx, _ = op.dispatch(x, wts, sc, idx)
             comb = op.combine_scatter if args.combine == "scatter" else op.combine
             return comb(out if identity else c_in, out_w, out_idx)
-        _, u_w, _, _, _ = op.dispatch_dedup(x, wts, None, idx)
+        _, u_w, _, _, _ = op.dispatch_dedup(x, wts, sc, idx)
         e_out, e_w, _, _, _ = op.units_to_experts()
         op.experts_to_units(e_out if identity else c_in, e_w)
         return op.combine_units(None, u_w)
@@ -378,12 +396,16 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"none": "bf16", "fp8_e4m3_b128": "bf16->e4m3 (fp32 scales), fp32 combine",
-                  "mxfp4_b32": "bf16->e2m1 (e8m0 scales), fp32 combine"}[w.quant],
+        "dtype": ("u8 rows + fp32 scales carried, bf16 fp32-accumulated combine" if raw else
+                  {"none": "bf16", "fp8_e4m3_b128": "bf16->e4m3 (fp32 scales), fp32 combine",
+                   "mxfp4_b32": "bf16->e2m1 (e8m0 scales), fp32 combine"}[w.quant]),
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.tokens, "hidden": w.hidden, "topk": w.topk,
                    "experts": w.experts, "ranks": w.ranks, "routing": f"{w.routing}{w.zipf_s or ''}",
                    "quant": w.quant,
+                   "input": (f"pre-quantized rows of {w.raw_row_bytes} B + "
+                             f"{w.scale_row_bytes} B of fp32 scales, carried" if raw
+                             else "bf16 rows"),
                    "combine_input": "identity (dispatch output)" if identity
                    else "independent N(0,1) bf16 rows",
                    "graph_mode": "hip graph replay" if args.graph else "eager",
@@ -412,11 +434,11 @@ def main() -> int:
     if args.cpu_seconds > 0:
         if dedup:
             payload = op.received_unit_payload().view(torch.uint8).cpu().numpy()
-            scales = op.received_unit_scales(False)
+            scales = op.received_unit_scales(raw)
             scales = None if scales is None else scales.view(torch.uint8).cpu().numpy()
         else:
             payload = op.received_payload().view(torch.uint8).cpu().numpy()
-            scales = op.received_scales(False)
+            scales = op.received_scales(raw)
             scales = None if scales is None else scales.view(torch.uint8).cpu().numpy()
         combined = y.view(torch.int16).cpu().numpy().view(np.uint16)
         result["cpu_baseline"], parity = cpu_baseline(w, inp, args.cpu_seconds, payload, scales,

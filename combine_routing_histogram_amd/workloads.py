@@ -12,8 +12,9 @@ restrictions list): DeepSeek-V3-like (hidden 7168, 256 experts, top-8) and
 Qwen3-MoE-like (hidden 4096, 128 experts, top-8) layers, plus a tiny case and
 decode-sized cases.  No dataset or trained weights are involved.
 
-Recipe (all numpy PCG64, one SeedSequence per workload spawned into five
-independent streams: x, routing, logits, outliers, combine input):
+Recipe (all numpy PCG64, one SeedSequence per workload spawned into six
+independent streams: x, routing, logits, outliers, combine input, carried
+scales):
   * x: N(0,1) float32 -> bfloat16 with round-to-nearest-even (torch CPU cast);
     for the Qwen-like case 1% of elements (Bernoulli mask) are multiplied by 20
     before the cast.
@@ -22,8 +23,12 @@ independent streams: x, routing, logits, outliers, combine input):
     p_j ~ (j+1)^-s over popularity ranks j, where rank j is expert perm[j] for a
     seeded permutation perm.  Row order = draw order.
   * weights: float32 softmax over K N(0,1) logits per token.
-  * combine input (quantized workloads only): independent N(0,1) bfloat16 rows
-    in the received layout [T*K, H].
+  * combine input (quantized and pre-quantized workloads): independent N(0,1)
+    bfloat16 rows in the received layout [T*K, H].
+  * pre-quantized rows (raw workloads, payloads quantized before dispatch and
+    carried unchanged): uniform random bytes [T, raw_row_bytes] drawn from
+    the x stream (dispatch treats them as opaque), and per-token fp32 scale
+    rows |N(0,1)|/448 [T, scale_row_bytes/4].
 """
 from __future__ import annotations
 
@@ -48,6 +53,8 @@ class Workload:
     outlier_mult: float = 1.0
     combine_input: str = "identity"  # "identity" (dispatch output) or "independent"
     seed: int = 0
+    raw_row_bytes: int = 0    # > 0: pre-quantized byte rows carried unchanged
+    scale_row_bytes: int = 0  # bytes of the fp32 scale row carried with each raw row
 
     @property
     def pairs(self) -> int:
@@ -66,6 +73,11 @@ WORKLOADS: Dict[str, Workload] = {
         Workload("qwen3_moe_mxfp4", 16384, 4096, 8, 128, 8, "zipf", zipf_s=1.3,
                  quant="mxfp4_b32", outlier_frac=0.01, outlier_mult=20.0,
                  combine_input="independent", seed=1005),
+        # DeepSeek-V3 shape and routing with FP8 payloads quantized before
+        # dispatch: 7168-byte rows and 56 fp32 block scales carried as is
+        Workload("deepseek_v3_raw_fp8", 4096, 7168, 8, 256, 8, "zipf", zipf_s=1.1,
+                 combine_input="independent", seed=1002, raw_row_bytes=7168,
+                 scale_row_bytes=224),
     ]
 }
 
@@ -109,26 +121,36 @@ def make_inputs(w: Workload, tokens: Optional[int] = None,
                 with_combine_input: Optional[bool] = None) -> Dict[str, np.ndarray]:
     """Draw the inputs of workload ``w``.
 
-    Returns numpy arrays: ``x`` uint16 [T,H] (bf16 bits), ``indices`` int32
-    [T,K], ``weights`` float32 [T,K] and, when requested (default: when the
-    workload's combine input is independent), ``combine_input`` uint16
-    [T*K,H] (bf16 bits).  ``tokens`` overrides T (a prefix-sized draw with the
-    same recipe; it is a different draw, not a slice).
+    Returns numpy arrays: ``x`` uint16 [T,H] (bf16 bits) — uint8
+    [T,raw_row_bytes] for a raw workload, which also returns ``scales``
+    float32 [T,scale_row_bytes/4] — ``indices`` int32 [T,K], ``weights``
+    float32 [T,K] and, when requested (default: when the workload's combine
+    input is independent), ``combine_input`` uint16 [T*K,H] (bf16 bits).
+    ``tokens`` overrides T (a prefix-sized draw with the same recipe; it is a
+    different draw, not a slice).
     """
     T = w.tokens if tokens is None else int(tokens)
     ss = np.random.SeedSequence(w.seed)
-    s_x, s_route, s_logit, s_out, s_comb = ss.spawn(5)
-    x = np.random.default_rng(s_x).standard_normal((T, w.hidden), dtype=np.float32)
-    if w.outlier_frac > 0.0:
-        mask = np.random.default_rng(s_out).random((T, w.hidden)) < w.outlier_frac
-        x[mask] *= np.float32(w.outlier_mult)
-    out = {
-        "x": f32_to_bf16_bits(x),
-        "indices": draw_topk(np.random.default_rng(s_route), T, w.experts, w.topk,
-                             w.routing, w.zipf_s),
-        "weights": softmax_weights(np.random.default_rng(s_logit), T, w.topk),
-    }
-    del x
+    # children depend only on their index: the sixth stream leaves the
+    # first five, and so every other workload's inputs, unchanged
+    s_x, s_route, s_logit, s_out, s_comb, s_scale = ss.spawn(6)
+    out = {}
+    if w.raw_row_bytes > 0:
+        out["x"] = np.random.default_rng(s_x).integers(0, 256, (T, w.raw_row_bytes),
+                                                      dtype=np.uint8)
+        sc = np.abs(np.random.default_rng(s_scale).standard_normal(
+            (T, w.scale_row_bytes // 4), dtype=np.float32)) / np.float32(448.0)
+        out["scales"] = np.ascontiguousarray(sc, dtype=np.float32)
+    else:
+        x = np.random.default_rng(s_x).standard_normal((T, w.hidden), dtype=np.float32)
+        if w.outlier_frac > 0.0:
+            mask = np.random.default_rng(s_out).random((T, w.hidden)) < w.outlier_frac
+            x[mask] *= np.float32(w.outlier_mult)
+        out["x"] = f32_to_bf16_bits(x)
+        del x
+    out["indices"] = draw_topk(np.random.default_rng(s_route), T, w.experts, w.topk,
+                               w.routing, w.zipf_s)
+    out["weights"] = softmax_weights(np.random.default_rng(s_logit), T, w.topk)
     if with_combine_input is None:
         with_combine_input = w.combine_input == "independent"
     if with_combine_input:

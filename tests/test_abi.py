@@ -40,6 +40,9 @@ def _cfg(w, **kw):
     q = {"none": 0, "fp8_e4m3_b128": 1, "mxfp4_b32": 2}[w.quant]
     args = dict(max_tokens=w.tokens, hidden=w.hidden, topk=w.topk, num_experts=w.experts,
                 num_ranks=w.ranks, quant=q)
+    if w.raw_row_bytes:
+        args.update(input_kind=B.EPDC_IN_RAW, raw_row_bytes=w.raw_row_bytes,
+                    scale_row_bytes=w.scale_row_bytes)
     args.update(kw)
     return B.make_config(**args)
 
@@ -56,6 +59,8 @@ def test_workspace_and_row_bytes(lib, name):
     p, s = B.epdc_row_bytes(c)
     want = {"none": (2 * w.hidden, 0), "fp8_e4m3_b128": (w.hidden, 4 * w.hidden // 128),
             "mxfp4_b32": (w.hidden // 2, w.hidden // 32)}[w.quant]
+    if w.raw_row_bytes:
+        want = (w.raw_row_bytes, w.scale_row_bytes)
     assert (p, s) == want
 
 

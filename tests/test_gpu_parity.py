@@ -119,15 +119,17 @@ def run_case(x, weights, indices, E, R, quant="none", max_tokens=None, hidden=No
 # ---- the workloads at their full sizes ---------------------------------------------
 
 @pytest.mark.parametrize("name", ["tiny_bf16", "decode_sparse_bf16", "decode_bf16",
-                                  "deepseek_v3_bf16", "deepseek_v3_fp8", "qwen3_moe_mxfp4"])
+                                  "deepseek_v3_bf16", "deepseek_v3_fp8", "qwen3_moe_mxfp4",
+                                  "deepseek_v3_raw_fp8"])
 def test_workload_parity(name):
     w = wl.WORKLOADS[name]
     log(f"workload {name}: T={w.tokens} H={w.hidden} K={w.topk} E={w.experts} R={w.ranks} "
-        f"quant={w.quant}")
+        f"quant={w.quant} raw_row_bytes={w.raw_row_bytes}")
     inp = inputs_for(name)
     c_in = inp["combine_input"] if w.combine_input == "independent" else None
     run_case(inp["x"], inp["weights"], inp["indices"], w.experts, w.ranks, quant=w.quant,
-             combine_input=c_in)
+             combine_input=c_in, hidden=w.hidden, raw_row_bytes=w.raw_row_bytes,
+             scales=inp.get("scales"))
 
 
 # ---- ragged and edge cases ----------------------------------------------------------------
