@@ -421,7 +421,10 @@ def main() -> int:
             "step_frac_of_copy": step_bytes / (ms_step * 1e-3) / 1e9 / copy_gbps},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": dk["gbps"],
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": dk["frac"],
-                     "traffic": traffic},
+                     "traffic": traffic,
+                     # the same kernel against the device copy measured in this run
+                     "frac_of_copy": None if copy_gbps is None or not dk["gbps"]
+                     else dk["gbps"] / copy_gbps},
         "kernels": kernels,
         "ms_per_step_events": ms_step_events,
         "kernel_events": args.kernel_events,
