@@ -39,11 +39,28 @@
  * multiply and add, starting from +0.0f, then rounds to bf16 to nearest even.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -shared -fPIC (no fast-math).
+ * A second build of the same source adds -fopenmp: the loops over tokens
+ * marked "omp parallel for" below then run on all host cores.  Each token's
+ * iteration writes only its own rows (distinct slots; the routing's cursor
+ * loop stays serial), so both builds give identical results.
  */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the token loops use: 1 in the plain build. */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ---- bfloat16: the top 16 bits of an IEEE binary32 ---------------------- */
 
@@ -195,6 +212,7 @@ int oracle_route(int T, int K, int E, int R, const int32_t *indices,
 void oracle_scatter_rows(int T, int K, const int32_t *slot_of,
                          const uint8_t *src, long row_bytes, uint8_t *dst)
 {
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t)
         for (int k = 0; k < K; ++k) {
             int32_t s = slot_of[(long)t * K + k];
@@ -213,6 +231,7 @@ int oracle_quant_fp8(int T, int H, const uint16_t *x, uint8_t *q, float *scales)
     const int B = 128;
     if (H % B != 0)
         return -1;
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t)
         for (int j = 0; j < H / B; ++j) {
             const uint16_t *xb = x + (long)t * H + (long)j * B;
@@ -248,6 +267,7 @@ int oracle_quant_mxfp4(int T, int H, const uint16_t *x, uint8_t *q, uint8_t *sca
     const int B = 32;
     if (H % B != 0)
         return -1;
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t)
         for (int j = 0; j < H / B; ++j) {
             const uint16_t *xb = x + (long)t * H + (long)j * B;
@@ -293,8 +313,9 @@ void oracle_combine(int T, int H, int K, const int32_t *slot_of,
                     const uint16_t *in, const float *weights,
                     uint16_t *out, float *out_weights)
 {
-    float *w = (float *)malloc(sizeof(float) * (size_t)K);
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; ++t) {
+        float *w = (float *)malloc(sizeof(float) * (size_t)K);
         for (int k = 0; k < K; ++k) {
             int32_t s = slot_of[(long)t * K + k];
             w[k] = (s < 0) ? 0.0f : (weights ? weights[(long)s * K + k] : 1.0f);
@@ -312,8 +333,8 @@ void oracle_combine(int T, int H, int K, const int32_t *slot_of,
             }
             out[(long)t * H + h] = f32_to_bf16_rne(acc);
         }
+        free(w);
     }
-    free(w);
 }
 
 /* ---- scatter combine: experts push, the token side reduces -------------- */

@@ -1,7 +1,8 @@
 """CPU oracle for MoE dispatch/combine -- TEST INFRASTRUCTURE ONLY.
 
 Thin numpy/ctypes front end of ``epdc_oracle.c`` (plain C loops, single
-thread).  Only ``tests/``, the smoke check and the benchmark's CPU-baseline
+thread; a second build of the same source with OpenMP runs the loops over
+tokens on all host cores, selected with ``use_openmp``).  Only ``tests/``, the smoke check and the benchmark's CPU-baseline
 leg may import this module; the product path never does, and the HIP library
 shares no code with it.  See the C file's header for the passages of the MORI
 pages each step follows.
@@ -24,31 +25,56 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "epdc_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
-_lib = None
+_OMP_LIB_PATH = os.path.join(_HERE, "liboracle_omp.so")
+_libs = {}
+_variant = "plain"
 
-GCC_CMD = ["gcc", "-O2", "-std=c11", "-Wall", "-ffp-contract=off", "-shared", "-fPIC", _SRC]
+GCC_CMD = ["gcc", "-O2", "-std=c11", "-Wall", "-Wno-unknown-pragmas", "-ffp-contract=off",
+           "-shared", "-fPIC", _SRC]
+
+
+def _build_one(path: str, extra) -> str:
+    tmp = path + ".tmp"
+    subprocess.run(GCC_CMD + list(extra) + ["-o", tmp, "-lm"], check=True)
+    os.replace(tmp, path)
+    return path
 
 
 def build() -> str:
-    """Compile the oracle library in place (plain gcc, no fast-math)."""
-    tmp = _LIB_PATH + ".tmp"
-    cmd = GCC_CMD + ["-o", tmp, "-lm"]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    """Compile the oracle library in place (plain gcc, no fast-math), and
+    the OpenMP build of the same source beside it."""
+    _build_one(_OMP_LIB_PATH, ["-fopenmp"])
+    return _build_one(_LIB_PATH, [])
+
+
+def use_openmp(on: bool = True) -> int:
+    """Route every oracle call to the OpenMP build (on) or the plain
+    single-thread build (off).  Returns the threads the token loops use."""
+    global _variant
+    _variant = "openmp" if on else "plain"
+    return int(_load().oracle_num_threads())
+
+
+def _stale(path: str) -> bool:
+    return not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC)
 
 
 def _load():
-    global _lib
-    if _lib is not None:
-        return _lib
-    # EPDC_ORACLE_LIB: a separately built copy of the oracle (the mutation
-    # tests build copies with planted mistakes and run the pins against them)
-    path = os.environ.get("EPDC_ORACLE_LIB")
-    if not path:
-        path = _LIB_PATH
-        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
-            build()
+    lib = _libs.get(_variant)
+    if lib is not None:
+        return lib
+    if _variant == "openmp":
+        path = _OMP_LIB_PATH
+        if _stale(path):
+            _build_one(path, ["-fopenmp"])
+    else:
+        # EPDC_ORACLE_LIB: a separately built copy of the oracle (the mutation
+        # and sanitizer tests build copies and run the pins against them)
+        path = os.environ.get("EPDC_ORACLE_LIB")
+        if not path:
+            path = _LIB_PATH
+            if _stale(path):
+                _build_one(path, [])
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     I = ctypes.c_int
@@ -73,7 +99,9 @@ def _load():
     lib.oracle_e4m3_encode_array.argtypes = [L, P, P]
     lib.oracle_e2m1_encode_array.argtypes = [L, P, P]
     lib.oracle_f32_to_bf16_array.argtypes = [L, P, P]
-    _lib = lib
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = I
+    _libs[_variant] = lib
     return lib
 
 
