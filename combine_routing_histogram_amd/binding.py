@@ -42,7 +42,10 @@ EPDC_KERNEL_EXPERTS_TO_UNITS = 7
 EPDC_KERNEL_COMBINE_UNITS = 8
 EPDC_KERNEL_COMBINE_PUSH = 9
 EPDC_KERNEL_COMBINE_REDUCE = 10
-EPDC_NUM_KERNELS = 11
+EPDC_KERNEL_CHECK_INDICES = 11
+EPDC_NUM_KERNELS = 12
+
+EPDC_DEBUG_CHECK_INDICES = 1
 
 
 class epdc_config(ctypes.Structure):
@@ -79,6 +82,8 @@ _SIGNATURES = {
     "epdc_combine_recv": (I32, [P, P]),
     "epdc_get_dispatch_src_token_pos": (I32, [P, ctypes.POINTER(P), PI32]),
     "epdc_get_routing": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P)]),
+    "epdc_get_offsets": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(P)]),
+    "epdc_set_debug": (I32, [P, I32]),
     "epdc_combine_scatter": (I32, [P, P, P, P, P, P, P, P]),
     "epdc_dispatch_dedup": (I32, [P, P, I32, P, P, P, P, P, P, P, P, P]),
     "epdc_get_unit_routing": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P)]),
@@ -211,6 +216,16 @@ def epdc_get_routing(op: int) -> Tuple[int, int, int]:
     a, b, c = P(None), P(None), P(None)
     _check(lib().epdc_get_routing(op, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
     return a.value, b.value, c.value
+
+
+def epdc_get_offsets(op: int) -> Tuple[int, int]:
+    a, b = P(None), P(None)
+    _check(lib().epdc_get_offsets(op, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def epdc_set_debug(op: int, flags: int) -> None:
+    _check(lib().epdc_set_debug(op, flags))
 
 
 def epdc_combine_scatter(op: int, stream: int, input: int, weights: int, indices: int,

@@ -170,7 +170,7 @@ void row_bytes_for(const epdc_config &c, size_t *payload, size_t *scales)
 const char *const kKernelNames[EPDC_NUM_KERNELS] = {
     "k_route_rank", "k_route_scan", "k_scatter_copy", "k_scatter_fp8", "k_scatter_mxfp4",
     "k_combine", "k_units_to_experts", "k_experts_to_units", "k_combine_units",
-    "k_combine_push", "k_combine_reduce"};
+    "k_combine_push", "k_combine_reduce", "k_check_indices"};
 
 }  // namespace
 
@@ -184,7 +184,8 @@ struct epdc_op {
     bool routed;
     bool units_routed;  // the last dispatch was rank-deduplicated
     int32_t last_tokens;
-    // split-phase completion markers (timing disabled)
+    int32_t debug;          // EPDC_DEBUG_* bits (epdc_set_debug)
+    // split-phase completion markers (timing disabled), made on first use
     hipEvent_t ev_dispatch, ev_combine;
     bool dispatch_sent, combine_sent;
     // per-kernel timing
@@ -492,6 +493,28 @@ epdc_status launch_combine_mode(epdc_op *op, hipStream_t st, int kernel_id, Comb
     });
 }
 
+// The debug check of combine's indices (k_check_indices), when the op has it
+// switched on and the caller passed indices.
+epdc_status check_combine_indices(epdc_op *op, hipStream_t st, const int32_t *indices)
+{
+    if (!(op->debug & EPDC_DEBUG_CHECK_INDICES) || !indices)
+        return EPDC_SUCCESS;
+    if (!aligned(indices, 4))
+        return fail(EPDC_ERR_INVALID_ARGS, "indices must be 4-byte aligned");
+    const epdc_config &c = op->cfg;
+    CheckArgs ca = {};
+    ca.n_pairs = op->last_tokens * c.topk;
+    ca.topk = c.topk;
+    ca.num_experts = c.num_experts;
+    ca.expert_off = op->i32(op->lay.expert_off);
+    ca.src_pos = op->i32(op->lay.src_pos);
+    ca.indices = indices;
+    ca.ctrl = op->ctrl();
+    const int grid = (ca.n_pairs + 255) / 256;
+    return launch(op, st, EPDC_KERNEL_CHECK_INDICES,
+                  [&] { k_check_indices<<<grid, 256, 0, st>>>(ca); });
+}
+
 }  // namespace
 
 extern "C" {
@@ -518,21 +541,14 @@ epdc_status epdc_row_bytes(const epdc_config *cfg, size_t *payload_bytes, size_t
     return ok();
 }
 
-epdc_status epdc_create(const epdc_config *cfg, void *workspace, size_t workspace_bytes,
-                        epdc_op **op)
+}  // extern "C"
+
+namespace {
+
+// Create an op on the current device over `workspace` (>= layout total bytes).
+epdc_status create_on(const epdc_config *cfg, void *workspace, epdc_op **op)
 {
-    epdc_status s = check_config(cfg);
-    if (s != EPDC_SUCCESS)
-        return s;
-    if (!op)
-        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
-    *op = nullptr;
     const Layout lay = layout_for(*cfg);
-    if (!workspace || ((uintptr_t)workspace & 255u) != 0)
-        return fail(EPDC_ERR_INVALID_ARGS, "workspace must be a 256-byte aligned device pointer");
-    if (workspace_bytes < lay.total)
-        return fail(EPDC_ERR_INVALID_ARGS, "workspace has %zu bytes, needs %zu", workspace_bytes,
-                    lay.total);
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
@@ -544,26 +560,16 @@ epdc_status epdc_create(const epdc_config *cfg, void *workspace, size_t workspac
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
         return fail(EPDC_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950",
                     dev, prop.gcnArchName);
+    // the sticky error flag and the other control words start at zero
     e = hipMemset(static_cast<uint8_t *>(workspace) + lay.ctrl, 0, sizeof(uint32_t) * kCtrlWords);
     if (e == hipSuccess)
         e = hipDeviceSynchronize();
     if (e != hipSuccess)
         return fail(EPDC_ERR_GPU_OP, "clearing control words: %s", hipGetErrorString(e));
 
-    hipEvent_t ev_d = nullptr, ev_c = nullptr;
-    e = hipEventCreateWithFlags(&ev_d, hipEventDisableTiming);
-    if (e == hipSuccess)
-        e = hipEventCreateWithFlags(&ev_c, hipEventDisableTiming);
-    if (e != hipSuccess) {
-        if (ev_d)
-            (void)hipEventDestroy(ev_d);
-        return fail(EPDC_ERR_GPU_OP, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
-    }
-
     epdc_op *o = new epdc_op();
     o->cfg = *cfg;
-    o->ev_dispatch = ev_d;
-    o->ev_combine = ev_c;
+    o->ev_dispatch = o->ev_combine = nullptr;
     o->dispatch_sent = o->combine_sent = false;
     o->device = dev;
     o->ws = static_cast<uint8_t *>(workspace);
@@ -579,10 +585,46 @@ epdc_status epdc_create(const epdc_config *cfg, void *workspace, size_t workspac
     o->routed = false;
     o->units_routed = false;
     o->last_tokens = 0;
+    o->debug = 0;
     o->profiling = false;
     o->ev_cap = o->ev_used = 0;
     *op = o;
     return ok();
+}
+
+// The split phases' completion marker, created on the first send.
+epdc_status send_event(hipEvent_t *ev)
+{
+    if (*ev)
+        return EPDC_SUCCESS;
+    const hipError_t e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        *ev = nullptr;
+        return fail(EPDC_ERR_GPU_OP, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
+    }
+    return EPDC_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+epdc_status epdc_create(const epdc_config *cfg, void *workspace, size_t workspace_bytes,
+                        epdc_op **op)
+{
+    epdc_status s = check_config(cfg);
+    if (s != EPDC_SUCCESS)
+        return s;
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    *op = nullptr;
+    const Layout lay = layout_for(*cfg);
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0)
+        return fail(EPDC_ERR_INVALID_ARGS, "workspace must be a 256-byte aligned device pointer");
+    if (workspace_bytes < lay.total)
+        return fail(EPDC_ERR_INVALID_ARGS, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                    lay.total);
+    return create_on(cfg, workspace, op);
 }
 
 epdc_status epdc_destroy(epdc_op *op)
@@ -591,8 +633,10 @@ epdc_status epdc_destroy(epdc_op *op)
         return ok();
     for (hipEvent_t ev : op->ev)
         (void)hipEventDestroy(ev);
-    (void)hipEventDestroy(op->ev_dispatch);
-    (void)hipEventDestroy(op->ev_combine);
+    if (op->ev_dispatch)
+        (void)hipEventDestroy(op->ev_dispatch);
+    if (op->ev_combine)
+        (void)hipEventDestroy(op->ev_combine);
     delete op;
     return ok();
 }
@@ -959,7 +1003,6 @@ epdc_status epdc_combine_units(epdc_op *op, void *stream, const void *input,
 epdc_status epdc_combine(epdc_op *op, void *stream, const void *input, const float *weights,
                          const int32_t *indices, void *output, float *out_weights)
 {
-    (void)indices;  // the op keeps the routing of the last dispatch
     if (!op)
         return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
     if (!op->routed)
@@ -975,6 +1018,10 @@ epdc_status epdc_combine(epdc_op *op, void *stream, const void *input, const flo
         return fail(EPDC_ERR_INVALID_ARGS,
                     "input/output must be 16-byte aligned, weights 4-byte aligned");
 
+    // the op keeps the routing of the last dispatch; indices are only checked
+    epdc_status s = check_combine_indices(op, static_cast<hipStream_t>(stream), indices);
+    if (s != EPDC_SUCCESS)
+        return s;
     CombineArgs ca = {};
     ca.slot_of = op->i32(op->lay.slot_of);
     ca.input = static_cast<const uint8_t *>(input);
@@ -982,8 +1029,8 @@ epdc_status epdc_combine(epdc_op *op, void *stream, const void *input, const flo
     ca.output = static_cast<uint8_t *>(output);
     ca.out_weights = out_weights;
     ca.xcd_order = one_tile_xcd_order((int64_t)T * c.topk);
-    const epdc_status s = launch_combine_mode<kCombinePairs>(
-        op, static_cast<hipStream_t>(stream), EPDC_KERNEL_COMBINE, ca, T);
+    s = launch_combine_mode<kCombinePairs>(op, static_cast<hipStream_t>(stream),
+                                           EPDC_KERNEL_COMBINE, ca, T);
     return s == EPDC_SUCCESS ? ok() : s;
 }
 
@@ -991,7 +1038,6 @@ epdc_status epdc_combine_scatter(epdc_op *op, void *stream, const void *input,
                                  const float *weights, const int32_t *indices, float *staging,
                                  void *output, float *out_weights)
 {
-    (void)indices;  // the op keeps the routing of the last dispatch
     if (!op)
         return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
     if (!op->routed)
@@ -1006,6 +1052,11 @@ epdc_status epdc_combine_scatter(epdc_op *op, void *stream, const void *input,
         !aligned(weights, 4) || !aligned(out_weights, 4))
         return fail(EPDC_ERR_INVALID_ARGS,
                     "input/staging/output must be 16-byte aligned, weights 4-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // the op keeps the routing of the last dispatch; indices are only checked
+    epdc_status s = check_combine_indices(op, st, indices);
+    if (s != EPDC_SUCCESS)
+        return s;
     constexpr int CH = kCombineSeg;
     PushArgs pa = {};
     pa.rows = T * c.topk;
@@ -1023,9 +1074,8 @@ epdc_status epdc_combine_scatter(epdc_op *op, void *stream, const void *input,
     pa.out_weights = out_weights;
     pa.num_tokens = T;
     pa.cached_stores = (int64_t)pa.n_pairs * c.hidden * 4 <= kL2ResidentBytes;
-    hipStream_t st = static_cast<hipStream_t>(stream);
     int grid, block;
-    epdc_status s = grid_for_waves((int64_t)pa.rows * pa.segs, &grid, &block);
+    s = grid_for_waves((int64_t)pa.rows * pa.segs, &grid, &block);
     if (s == EPDC_SUCCESS)
         s = launch(op, st, EPDC_KERNEL_COMBINE_PUSH,
                    [&] { k_combine_push<CH><<<grid, block, 0, st>>>(pa); });
@@ -1109,8 +1159,13 @@ epdc_status epdc_dispatch_send(epdc_op *op, void *stream, int32_t num_tokens, co
                                void *out, float *out_weights, void *out_scales,
                                int32_t *out_indices, int32_t *recv_count)
 {
-    epdc_status s = epdc_dispatch(op, stream, num_tokens, input, weights, scales, indices, out,
-                                  out_weights, out_scales, out_indices, recv_count);
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    epdc_status s = send_event(&op->ev_dispatch);
+    if (s != EPDC_SUCCESS)
+        return s;
+    s = epdc_dispatch(op, stream, num_tokens, input, weights, scales, indices, out, out_weights,
+                      out_scales, out_indices, recv_count);
     if (s != EPDC_SUCCESS)
         return s;
     const hipError_t e = hipEventRecord(op->ev_dispatch, static_cast<hipStream_t>(stream));
@@ -1136,7 +1191,12 @@ epdc_status epdc_dispatch_recv(epdc_op *op, void *stream)
 epdc_status epdc_combine_send(epdc_op *op, void *stream, const void *input, const float *weights,
                               const int32_t *indices, void *output, float *out_weights)
 {
-    epdc_status s = epdc_combine(op, stream, input, weights, indices, output, out_weights);
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    epdc_status s = send_event(&op->ev_combine);
+    if (s != EPDC_SUCCESS)
+        return s;
+    s = epdc_combine(op, stream, input, weights, indices, output, out_weights);
     if (s != EPDC_SUCCESS)
         return s;
     const hipError_t e = hipEventRecord(op->ev_combine, static_cast<hipStream_t>(stream));
@@ -1183,6 +1243,21 @@ epdc_status epdc_get_routing(epdc_op *op, const int32_t **expert_off, const int3
         *rank_off = op->i32(op->lay.rank_off);
     if (slot_of)
         *slot_of = op->i32(op->lay.slot_of);
+    return ok();
+}
+
+epdc_status epdc_get_offsets(epdc_op *op, const int32_t **expert_off, const int32_t **rank_off)
+{
+    return epdc_get_routing(op, expert_off, rank_off, nullptr);
+}
+
+epdc_status epdc_set_debug(epdc_op *op, int32_t flags)
+{
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    if (flags & ~EPDC_DEBUG_CHECK_INDICES)
+        return fail(EPDC_ERR_INVALID_ARGS, "unknown debug flags 0x%x", (unsigned)flags);
+    op->debug = flags;
     return ok();
 }
 
@@ -1234,7 +1309,9 @@ epdc_status epdc_profile_begin(epdc_op *op, int32_t max_launches)
     op->ev.assign(2 * (size_t)max_launches, nullptr);
     op->ev_kernel.assign((size_t)max_launches, -1);
     for (auto &ev : op->ev) {
-        hipError_t e = hipEventCreate(&ev);
+        // no system-scope release at the timestamps: the write-back it does
+        // would be timed as part of the kernel it follows
+        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableSystemFence);
         if (e != hipSuccess) {
             op->profiling = false;
             return fail(EPDC_ERR_GPU_OP, "hipEventCreate: %s", hipGetErrorString(e));

@@ -1663,4 +1663,55 @@ __global__ __launch_bounds__(256) void k_combine_reduce(PushArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Debug check of combine's indices against the recorded routing
+// ---------------------------------------------------------------------------
+//
+// combine(input, weights, indices) takes the indices in the received layout
+// (MORI "Communication APIs" page, MORI-EP section, methods table).  The op
+// keeps the routing of the last dispatch, so the indices are redundant; when
+// the caller asks for the check, every received row s < n_valid must hold,
+// in entry k of its indices row, the expert that row belongs to, where k is
+// the k of the pair the row came from (src_pos[s] mod K) and the expert is
+// the one whose run of rows [expert_off[e], expert_off[e+1]) contains s.
+// A mismatch raises bit 4 of the device error flag; the check writes
+// nothing else.  One thread per row of the capacity of the call.
+
+struct CheckArgs {
+    int32_t n_pairs;             // num_tokens * K of the recorded dispatch
+    int32_t topk;
+    int32_t num_experts;
+    const int32_t *expert_off;   // [E+1]
+    const int32_t *src_pos;      // [n_valid]
+    const int32_t *indices;      // [rows, K] received layout
+    uint32_t *ctrl;
+};
+
+__global__ __launch_bounds__(256) void k_check_indices(CheckArgs a)
+{
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    const int E = a.num_experts;
+    const int n_valid = a.expert_off[E];
+    if (s >= a.n_pairs || s >= n_valid)
+        return;
+    const int p = a.src_pos[s];
+    bool bad = (unsigned)p >= (unsigned)a.n_pairs;
+    if (!bad) {
+        // the expert e with expert_off[e] <= s < expert_off[e+1]: the last
+        // e in [0, E) whose first row is <= s (empty experts share an offset
+        // with the next one, so the last such e is the non-empty one)
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (a.expert_off[mid] <= s)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        bad = a.indices[(size_t)s * a.topk + p % a.topk] != lo;
+    }
+    if (bad)
+        atomicOr(&a.ctrl[kCtrlError], 4u);
+}
+
 }  // namespace epdc

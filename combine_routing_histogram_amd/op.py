@@ -427,10 +427,7 @@ class EpDispatchCombineOp:
             input, indices = ub["out"], ub["indices"]
             weights = ub["weights"] if has_w else None
             scales = ub["scales"] if (has_s or self.config.quant != "none") else None
-        for t, n in ((input, "input"), (weights, "weights"), (scales, "scales"),
-                     (indices, "indices")):
-            if t is not None:
-                self._need(t, n)
+        self._check_unit_rows(input, weights, scales, indices)
         B.epdc_units_to_experts(self._op, self._stream(), _ptr(input), _ptr(weights),
                                 _ptr(scales), _ptr(indices), _ptr(self._out),
                                 _ptr(self._out_weights) if weights is not None else 0,
@@ -438,6 +435,26 @@ class EpDispatchCombineOp:
                                 _ptr(self._out_indices) if indices is not None else 0)
         return (self.received_payload(), self._out_weights if weights is not None else None,
                 self.received_scales(scales is not None), self._out_indices, None)
+
+    def _check_unit_rows(self, input, weights, scales, indices) -> None:
+        """The conversion reads up to T * min(K, R) unit rows of each given
+        array (T of the last dispatch): check rows, row widths and dtypes on
+        the host so that no undersized tensor reaches the kernel."""
+        cfg = self.config
+        rows = self._tokens * min(cfg.topk, cfg.num_ranks)
+        for t, name, row_bytes, dtype in ((input, "input", self.payload_row_bytes, None),
+                                          (weights, "weights", 4 * cfg.topk, torch.float32),
+                                          (scales, "scales", self.scale_row_bytes, None),
+                                          (indices, "indices", 4 * cfg.topk, torch.int32)):
+            if t is None:
+                continue
+            self._need(t, name, dtype)
+            if t.dim() < 1 or t.shape[0] < rows:
+                raise ValueError(f"{name} needs at least {rows} unit rows, got "
+                                 f"{tuple(t.shape)}")
+            if t.shape[0] and (t.numel() // t.shape[0]) * t.element_size() != row_bytes:
+                raise ValueError(f"{name} rows must be {row_bytes} bytes, got "
+                                 f"{(t.numel() // t.shape[0]) * t.element_size()}")
 
     def experts_to_units(self, input: torch.Tensor,
                          weights: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -488,6 +505,17 @@ class EpDispatchCombineOp:
         cfg = self.config
         return (self._ws_view(a, cfg.num_experts + 1), self._ws_view(b, cfg.num_ranks + 1),
                 self._ws_view(c, self._tokens * cfg.topk))
+
+    def get_offsets(self):
+        """(expert_off [E+1], rank_off [R+1]) of the last dispatch."""
+        a, b = B.epdc_get_offsets(self._op)
+        cfg = self.config
+        return self._ws_view(a, cfg.num_experts + 1), self._ws_view(b, cfg.num_ranks + 1)
+
+    def set_debug(self, check_indices: bool = True) -> None:
+        """With check_indices, combine checks a given `indices` against the
+        recorded routing and raises bit 4 of the device error flag on a mismatch."""
+        B.epdc_set_debug(self._op, B.EPDC_DEBUG_CHECK_INDICES if check_indices else 0)
 
     def get_registered_combine_input_buffer(self, dtype=torch.bfloat16) -> torch.Tensor:
         """A capacity-sized [N_cap, H] buffer owned by the op, for expert outputs."""

@@ -119,7 +119,15 @@ enum {
     EPDC_KERNEL_COMBINE_UNITS = 8,    /* sum of a token's unit rows */
     EPDC_KERNEL_COMBINE_PUSH = 9,     /* scatter combine: weighted rows -> staging */
     EPDC_KERNEL_COMBINE_REDUCE = 10,  /* scatter combine: staging -> token rows */
-    EPDC_NUM_KERNELS = 11
+    EPDC_KERNEL_CHECK_INDICES = 11,   /* debug check of combine's indices */
+    EPDC_NUM_KERNELS = 12
+};
+
+/* Debug switches (epdc_set_debug). */
+enum {
+    /* combine and combine_scatter check a non-NULL `indices` against the
+     * recorded routing before combining (one extra launch) */
+    EPDC_DEBUG_CHECK_INDICES = 1
 };
 
 /* Bytes of device workspace an op with this config needs (host only, no GPU
@@ -180,8 +188,13 @@ epdc_status epdc_dispatch(epdc_op *op, void *stream, int32_t num_tokens,
  *   input       device [rows, H] bf16 in the received layout; only rows below
  *               n_valid <= num_tokens*K of the last dispatch are read
  *   weights     device [rows, K] fp32 in the received layout, or NULL
- *   indices     device [rows, K] int32 or NULL: accepted for signature
- *               parity with the pages and not read (the op keeps the routing)
+ *   indices     device [rows, K] int32 or NULL.  The op keeps the routing, so
+ *               combine does not need them; with EPDC_DEBUG_CHECK_INDICES on
+ *               (epdc_set_debug) a non-NULL `indices` is checked first: row
+ *               s < n_valid must hold, in entry k of its row (k of the pair
+ *               it came from), the expert whose rows contain s.  A mismatch
+ *               raises bit 4 of the device error flag (epdc_get_device_error)
+ *               and the combine still runs.
  *   output      device [num_tokens, H] bf16
  *   out_weights device [num_tokens, K] fp32 = w(t,k), or NULL
  * EPDC_ERR_BAD_STATE if no dispatch is recorded (none yet, or reset).
@@ -325,15 +338,29 @@ epdc_status epdc_combine_recv(epdc_op *op, void *stream);
 epdc_status epdc_get_dispatch_src_token_pos(epdc_op *op, const int32_t **dev_ptr,
                                             int32_t *count);
 
+/* Device pointers into the workspace for the last dispatch: expert_off [E+1]
+ * and rank_off [R+1] (exclusive prefix sums of the expert and rank counts;
+ * rank r's rows are [rank_off[r], rank_off[r+1])).  Either may be NULL.
+ * BAD_STATE if no dispatch is recorded. */
+epdc_status epdc_get_offsets(epdc_op *op, const int32_t **expert_off,
+                             const int32_t **rank_off);
+
 /* Device pointers into the workspace for the last dispatch: expert_off [E+1],
  * rank_off [R+1] (exclusive prefix sums), slot_of [num_tokens*K] (slot of
  * pair p, -1 if none).  Any may be NULL.  BAD_STATE if none. */
 epdc_status epdc_get_routing(epdc_op *op, const int32_t **expert_off,
                              const int32_t **rank_off, const int32_t **slot_of);
 
+/* Switch debug checks on or off for this op (EPDC_DEBUG_* bits; 0 = none,
+ * the default).  Host state only.  INVALID_ARGS for an unknown bit. */
+epdc_status epdc_set_debug(epdc_op *op, int32_t flags);
+
 /* Wait for `stream`, then return (host) and clear the sticky device error
- * flag: nonzero if some dispatch since the last call saw an expert id
- * outside [0, E).  Synchronizes; not for use under graph capture. */
+ * flag: nonzero if some call since the last read raised it.  Bits: 1 = a
+ * dispatch saw an expert id outside [0, E); 2 = a slot outside the call's
+ * rows (never produced by a consistent routing; the pair was dropped);
+ * 4 = the debug check found combine indices that disagree with the
+ * recorded routing.  Synchronizes; not for use under graph capture. */
 epdc_status epdc_get_device_error(epdc_op *op, void *stream, int32_t *flag);
 
 /* Forget the recorded routing and any unreceived send ("Reset internal state
@@ -348,8 +375,12 @@ const char *epdc_last_error(void);
 const char *epdc_kernel_name(int32_t kernel_id);
 
 /* Per-kernel timing with HIP events recorded on the launch stream around
- * each kernel the op launches.  begin: allocate events for up to
- * max_launches launches (host-side event objects, no device memory).  end:
+ * each kernel the op launches.  The events are created without the
+ * system-scope release at their timestamps (hipEventDisableSystemFence), so
+ * a pair times the launch, not an L2 write-back after it; they order
+ * nothing and make no memory visible to the host.  begin: allocate events
+ * for up to max_launches launches (host-side event objects, no device
+ * memory).  end:
  * wait for the last recorded event, write (host) the summed milliseconds and
  * the launch count per kernel id into ms[EPDC_NUM_KERNELS] and
  * launches[EPDC_NUM_KERNELS], and release the events. */

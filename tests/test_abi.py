@@ -115,7 +115,7 @@ def test_kernel_names(lib):
     assert names == ["k_route_rank", "k_route_scan", "k_scatter_copy", "k_scatter_fp8",
                      "k_scatter_mxfp4", "k_combine", "k_units_to_experts",
                      "k_experts_to_units", "k_combine_units", "k_combine_push",
-                     "k_combine_reduce"]
+                     "k_combine_reduce", "k_check_indices"]
     assert B.epdc_kernel_name(B.EPDC_NUM_KERNELS) is None
 
 
@@ -152,6 +152,8 @@ def test_every_entry_point_rejects_a_null_op(lib):
         lambda: B.epdc_experts_to_units(0, 0, 1, 0, 1),
         lambda: B.epdc_combine_units(0, 0, 1, 0, 1, 0),
         lambda: B.epdc_get_routing(0),
+        lambda: B.epdc_get_offsets(0),
+        lambda: B.epdc_set_debug(0, 1),
         lambda: B.epdc_get_dispatch_src_token_pos(0),
     ]
     for call in calls:
@@ -176,3 +178,32 @@ def test_header_is_plain_c(tmp_path):
                    + "int main(void) { return 0; }\n")
     subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
                     "-I", os.path.join(ROOT, "include"), str(src)], check=True)
+
+
+def test_unit_conversion_rejects_undersized_tensors():
+    """units_to_experts checks rows, widths and dtypes of caller tensors on the
+    host: the kernel reads up to T * min(K, R) rows of each."""
+    import torch
+
+    from combine_routing_histogram_amd.op import EpDispatchCombineConfig, EpDispatchCombineOp
+
+    op = EpDispatchCombineOp.__new__(EpDispatchCombineOp)   # host state only, no device
+    op.config = EpDispatchCombineConfig(16, 256, 4, 8, 2)
+    op.device = torch.device("cpu")
+    op._dev_index = -1
+    op._tokens = 10
+    op.payload_row_bytes, op.scale_row_bytes = 512, 0
+    rows = 10 * 2                                            # T * min(K, R)
+    good = dict(input=torch.zeros(rows, 256, dtype=torch.bfloat16),
+                weights=torch.zeros(rows, 4), scales=None,
+                indices=torch.zeros(rows, 4, dtype=torch.int32))
+    op._check_unit_rows(**good)
+    bad = [dict(good, input=torch.zeros(rows - 1, 256, dtype=torch.bfloat16)),
+           dict(good, input=torch.zeros(rows, 128, dtype=torch.bfloat16)),
+           dict(good, weights=torch.zeros(rows - 1, 4)),
+           dict(good, weights=torch.zeros(rows, 4, dtype=torch.float64)),
+           dict(good, indices=torch.zeros(rows, 3, dtype=torch.int32)),
+           dict(good, indices=torch.zeros(rows, 4, dtype=torch.int64))]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            op._check_unit_rows(**kw)

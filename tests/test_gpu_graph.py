@@ -2,9 +2,10 @@
 backend" page, "Validation before tuning": graph replay is one of the checks).
 
 The launches record no memset node (the kernels write every count and offset
-themselves), so a captured step can be replayed.  Each replay is checked
-against the eager result, with eager work that overwrites the outputs between
-replays.
+themselves), so a captured step can be replayed.  Every replay -- with eager
+work that overwrites all of the step's outputs between replays -- is compared
+bit for bit with the CPU oracle on the same inputs, and so is the eager step
+the graph was captured from.
 """
 import numpy as np
 import pytest
@@ -12,69 +13,36 @@ import torch
 
 from combine_routing_histogram_amd import workloads as wl
 from combine_routing_histogram_amd.op import EpDispatchCombineConfig, EpDispatchCombineOp
+from oracle import oracle
 
 pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda", 0)
 
 
-@pytest.mark.parametrize("name,tokens", [("decode_bf16", None), ("deepseek_v3_bf16", 1024),
-                                         ("deepseek_v3_fp8", 300)])
-def test_graph_replay_matches_eager(name, tokens):
-    w = wl.WORKLOADS[name]
-    print(f"graph replay {name} tokens={tokens}", flush=True)
-    inp = wl.make_inputs(w, tokens=tokens, with_combine_input=True)
-    T = inp["x"].shape[0]
-    x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(DEV)
-    idx = torch.from_numpy(inp["indices"]).to(DEV)
-    wts = torch.from_numpy(inp["weights"]).to(DEV)
-    c_in = (torch.from_numpy(inp["combine_input"].view(np.int16)).view(torch.bfloat16).to(DEV)
-            if w.combine_input == "independent" else None)
-    op = EpDispatchCombineOp(EpDispatchCombineConfig(T, w.hidden, w.topk, w.experts, w.ranks,
-                                                     quant=w.quant), DEV)
-
-    def step():
-        out, out_w, _, out_idx, recv = op.dispatch(x, wts, None, idx)
-        y, y_w = op.combine(out if c_in is None else c_in, out_w, out_idx)
-        return out, recv, y, y_w
-
-    out, recv, y, y_w = step()
-    torch.cuda.synchronize()
-    n = int(recv.sum())
-    ref = [out[:n].view(torch.uint8).clone(), recv.clone(), y.clone(), y_w.clone(),
-           op.get_dispatch_src_token_pos()[:n].clone()]
-
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step()
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        g_out, g_recv, g_y, g_yw = step()
-    torch.cuda.synchronize()
-
-    for rep in range(3):
-        # eager work between replays: clobber everything the replay must rewrite
-        g_out.view(torch.uint8).fill_(0xA5)
-        g_recv.fill_(-1)
-        g_y.fill_(3.0)
-        g_yw.fill_(-2.0)
-        op.get_dispatch_src_token_pos().fill_(-7)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        got = [g_out[:n].view(torch.uint8), g_recv, g_y, g_yw, op.get_dispatch_src_token_pos()[:n]]
-        for a, b in zip(got, ref):
-            assert torch.equal(a, b), f"replay {rep} differs from the eager step"
+def _bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
 
 
-def _replay_matches(step, clobber, n_rep=3):
-    """Run `step` eagerly, capture it, and check every replay (with the
-    outputs clobbered by eager work in between) against the eager result."""
-    ref = [t.clone() for t in step()]
+def _bytes(a):
+    """Host bytes of a device tensor or a numpy array, one row per leading index."""
+    if isinstance(a, torch.Tensor):
+        a = a.contiguous().view(torch.uint8).cpu().numpy()
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint8).reshape(a.shape[0], -1) if a.ndim > 1 else a.view(np.uint8)
+
+
+def _assert_oracle(outs, expected, what):
+    assert len(outs) == len(expected)
+    for i, (g, e) in enumerate(zip(outs, expected)):
+        np.testing.assert_array_equal(_bytes(g), _bytes(e), err_msg=f"{what}: output {i}")
+
+
+def _replay_against_oracle(step, expected, n_rep=3):
+    """Run `step` eagerly and check it against `expected` (oracle arrays);
+    capture it; check every replay, with the outputs clobbered by eager work
+    in between, against the same arrays."""
+    _assert_oracle(step(), expected, "eager")
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -88,87 +56,112 @@ def _replay_matches(step, clobber, n_rep=3):
     torch.cuda.synchronize()
     for rep in range(n_rep):
         for t in outs:
-            clobber(t)
+            t.view(torch.uint8).fill_(0x5A)   # eager work: clobber what the replay rewrites
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for a, b in zip(outs, ref):
-            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"replay {rep} differs"
+        _assert_oracle(outs, expected, f"replay {rep}")
 
 
-def _clobber(t):
-    t.view(torch.uint8).fill_(0x5A)
+def _inputs(name, tokens):
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w, tokens=tokens, with_combine_input=True)
+    T = inp["x"].shape[0]
+    op = EpDispatchCombineOp(EpDispatchCombineConfig(T, w.hidden, w.topk, w.experts, w.ranks,
+                                                     quant=w.quant), DEV)
+    dev = dict(x=_bf16(inp["x"]), idx=torch.from_numpy(inp["indices"]).to(DEV),
+               wts=torch.from_numpy(inp["weights"]).to(DEV), c_in=_bf16(inp["combine_input"]))
+    return w, inp, T, op, dev
+
+
+@pytest.mark.parametrize("name,tokens", [("decode_bf16", None), ("deepseek_v3_bf16", 1024),
+                                         ("deepseek_v3_fp8", 300)])
+def test_graph_replay_dispatch_combine(name, tokens):
+    """decode: one launch each; 1024 bf16 tokens: route + scatter with the
+    scan folded into the scatter blocks; 300 FP8 tokens: three routing tiles
+    and the quantizing scatter."""
+    w, inp, T, op, d = _inputs(name, tokens)
+    print(f"graph replay {name} T={T}", flush=True)
+    identity = w.combine_input == "identity"
+    ref = oracle.dispatch(inp["x"], inp["weights"], inp["indices"], w.experts, w.ranks,
+                          quant=w.quant)
+    n = ref["n_valid"]
+    c_host = ref["out"] if identity else inp["combine_input"]
+    ry, ry_w = oracle.combine(c_host, ref["out_weights"], ref["slot_of"], T, w.topk)
+    expected = [ref["recv_count"], ref["out"], ref["out_weights"], ref["out_indices"],
+                ref["src_token_pos"], ry, ry_w]
+    if ref["out_scales"] is not None:
+        expected.append(ref["out_scales"])
+
+    def step():
+        out, out_w, out_s, out_idx, recv = op.dispatch(d["x"], d["wts"], None, d["idx"])
+        y, y_w = op.combine(out if identity else d["c_in"], out_w, out_idx)
+        got = [recv, out[:n], out_w[:n], out_idx[:n], op.get_dispatch_src_token_pos()[:n],
+               y, y_w]
+        if out_s is not None:
+            got.append(out_s[:n])
+        return got
+
+    _replay_against_oracle(step, expected)
 
 
 @pytest.mark.parametrize("name,tokens", [("decode_bf16", None), ("deepseek_v3_bf16", 1024),
                                          ("qwen3_moe_mxfp4", 300)])
 def test_graph_replay_dedup_pipeline(name, tokens):
-    w = wl.WORKLOADS[name]
-    print(f"graph dedup {name} tokens={tokens}", flush=True)
-    inp = wl.make_inputs(w, tokens=tokens, with_combine_input=True)
-    T = inp["x"].shape[0]
-    x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(DEV)
-    idx = torch.from_numpy(inp["indices"]).to(DEV)
-    wts = torch.from_numpy(inp["weights"]).to(DEV)
-    c_in = torch.from_numpy(inp["combine_input"].view(np.int16)).view(torch.bfloat16).to(DEV)
-    op = EpDispatchCombineOp(EpDispatchCombineConfig(T, w.hidden, w.topk, w.experts, w.ranks,
-                                                     quant=w.quant), DEV)
+    """Rank-deduplicated dispatch, conversion to the expert layout, conversion
+    back and unit combine, captured as one graph."""
+    w, inp, T, op, d = _inputs(name, tokens)
+    print(f"graph dedup {name} T={T}", flush=True)
+    ref = oracle.dispatch_dedup(inp["x"], inp["weights"], inp["indices"], w.experts, w.ranks,
+                                quant=w.quant)
+    U, n = ref["units"], ref["n_valid"]
+    pair = oracle.dispatch(inp["x"], inp["weights"], inp["indices"], w.experts, w.ranks,
+                           quant=w.quant)
+    part = oracle.experts_to_units(inp["combine_input"], pair["out_weights"], ref["unit_src"],
+                                   ref["unit_of"], ref["slot_of"], w.topk)
+    ry, ry_w = oracle.combine_units(part, ref["out_weights"], ref["unit_of"], T, w.topk)
+    expected = [ref["recv_count"], ref["out"], pair["out"], part, ry, ry_w]
 
-    _, _, _, _, recv = op.dispatch_dedup(x, wts, None, idx)
-    torch.cuda.synchronize()
-    U = int(recv.sum())
-    n = int(op.get_routing()[0][-1])
-
-    def step():  # only the rows a step writes are compared
-        u_out, u_w, _, _, recv = op.dispatch_dedup(x, wts, None, idx)
+    def step():
+        u_out, u_w, _, _, recv = op.dispatch_dedup(d["x"], d["wts"], None, d["idx"])
         e_out, e_w, _, _, _ = op.units_to_experts()
-        part = op.experts_to_units(c_in, e_w)
+        p = op.experts_to_units(d["c_in"], e_w)
         y, y_w = op.combine_units(None, u_w)
-        return [recv, u_out[:U], e_out[:n], part[:U], y, y_w]
+        return [recv, u_out[:U], e_out[:n], p[:U], y, y_w]
 
-    _replay_matches(step, _clobber)
+    _replay_against_oracle(step, expected)
 
 
 def test_graph_replay_scatter_combine():
-    w = wl.WORKLOADS["deepseek_v3_bf16"]
-    print("graph scatter combine", flush=True)
-    inp = wl.make_inputs(w, tokens=900)
-    T = inp["x"].shape[0]
-    x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(DEV)
-    idx = torch.from_numpy(inp["indices"]).to(DEV)
-    wts = torch.from_numpy(inp["weights"]).to(DEV)
-    op = EpDispatchCombineOp(EpDispatchCombineConfig(T, w.hidden, w.topk, w.experts, w.ranks),
-                             DEV)
-
-    _, _, _, _, recv = op.dispatch(x, wts, None, idx)
-    torch.cuda.synchronize()
-    n = int(recv.sum())
+    w, inp, T, op, d = _inputs("deepseek_v3_bf16", 900)
+    print(f"graph scatter combine T={T}", flush=True)
+    ref = oracle.dispatch(inp["x"], inp["weights"], inp["indices"], w.experts, w.ranks)
+    n = ref["n_valid"]
+    ry, ry_w, _ = oracle.combine_push(ref["out"], ref["out_weights"], ref["src_token_pos"],
+                                      ref["slot_of"], T, w.topk)
 
     def step():
-        out, out_w, _, out_idx, _ = op.dispatch(x, wts, None, idx)
+        out, out_w, _, out_idx, _ = op.dispatch(d["x"], d["wts"], None, d["idx"])
         y, y_w = op.combine_scatter(out, out_w, out_idx)
         return [out[:n], y, y_w]
 
-    _replay_matches(step, _clobber)
+    _replay_against_oracle(step, [ref["out"], ry, ry_w])
 
 
 def test_graph_replay_routing_replay():
-    w = wl.WORKLOADS["deepseek_v3_fp8"]
-    print("graph routing replay", flush=True)
-    inp = wl.make_inputs(w, tokens=700, with_combine_input=True)
-    T = inp["x"].shape[0]
-    x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(DEV)
-    x2 = (x.float() * 1.5).to(torch.bfloat16)
-    idx = torch.from_numpy(inp["indices"]).to(DEV)
-    wts = torch.from_numpy(inp["weights"]).to(DEV)
-    op = EpDispatchCombineOp(EpDispatchCombineConfig(T, w.hidden, w.topk, w.experts, w.ranks,
-                                                     quant=w.quant), DEV)
-    _, _, _, _, recv = op.dispatch(x, wts, None, idx)
+    w, inp, T, op, d = _inputs("deepseek_v3_fp8", 700)
+    print(f"graph routing replay T={T}", flush=True)
+    x2_host = wl.f32_to_bf16_bits(wl.bf16_bits_to_f32(inp["x"]) * np.float32(1.5))
+    x2 = _bf16(x2_host)
+    _, _, _, _, recv = op.dispatch(d["x"], d["wts"], None, d["idx"])
     torch.cuda.synchronize()
-    n = int(recv.sum())
+    ref = oracle.dispatch(x2_host, inp["weights"], inp["indices"], w.experts, w.ranks,
+                          quant=w.quant)
+    n = ref["n_valid"]
+    assert int(recv.sum()) == n
 
     def step():
-        out, out_w, out_s, _, _ = op.dispatch_replay(x2, wts)
+        out, out_w, out_s, _, _ = op.dispatch_replay(x2, d["wts"])
         return [out[:n], out_w[:n], out_s[:n]]
 
-    _replay_matches(step, _clobber)
+    _replay_against_oracle(step, [ref["out"], ref["out_weights"], ref["out_scales"]])

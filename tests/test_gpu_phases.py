@@ -186,3 +186,79 @@ def test_recv_without_send_is_an_error():
         with pytest.raises(B.EpdcError) as ei:
             fn(op._op, torch.cuda.current_stream(DEV).cuda_stream)
         assert ei.value.status == B.EPDC_ERR_BAD_STATE
+
+
+# ---- registered combine-input buffer ------------------------------------------------
+
+@pytest.mark.parametrize("name,tokens", [("deepseek_v3_bf16", 1500), ("decode_bf16", None)])
+def test_registered_combine_input_buffer(name, tokens):
+    """Expert outputs written into the op's registered buffer ("Communication
+    APIs" page, methods table: get_registered_combine_input_buffer) are
+    combined from it, bit-exact against the oracle's combine of the same rows."""
+    w = wl.WORKLOADS[name]
+    log(f"registered combine buffer {name} tokens={tokens}")
+    inp = wl.make_inputs(w, tokens=tokens, with_combine_input=True)
+    T, K = inp["indices"].shape
+    op = EpDispatchCombineOp(EpDispatchCombineConfig(T, w.hidden, K, w.experts, w.ranks), DEV)
+    _, out_w, _, out_idx, recv = op.dispatch(bf16_dev(inp["x"]),
+                                             torch.from_numpy(inp["weights"]).to(DEV), None,
+                                             torch.from_numpy(inp["indices"]).to(DEV))
+    buf = op.get_registered_combine_input_buffer()
+    assert buf.dtype == torch.bfloat16 and buf.shape == (T * K, w.hidden)
+    assert buf.data_ptr() == op.get_registered_combine_input_buffer().data_ptr()  # one buffer
+    with pytest.raises(ValueError):
+        op.get_registered_combine_input_buffer(torch.float32)
+    buf.copy_(bf16_dev(inp["combine_input"]))      # the "expert output"
+    y, y_w = op.combine(buf, out_w, out_idx)
+    torch.cuda.synchronize()
+    ref = oracle.dispatch(inp["x"], inp["weights"], inp["indices"], w.experts, w.ranks)
+    assert int(recv.sum()) == ref["n_valid"]
+    check_combine(y, y_w, inp["combine_input"], ref, T, K)
+
+
+# ---- debug check of combine's indices ------------------------------------------------
+
+@pytest.mark.parametrize("T", [700, 100])   # 5600 pairs: routing launches; 800: one launch
+def test_combine_indices_debug_check(T):
+    """With the debug check on, combine compares the given indices with the
+    recorded routing and raises bit 4 of the device error flag on a
+    mismatch; the combine itself still runs.  Off (the default), the indices
+    are not read."""
+    log(f"indices debug check T={T}")
+    rng = np.random.default_rng(T + 77)
+    H, K, E, R = 512, 8, 64, 8
+    x = wl.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    idx = wl.draw_topk(rng, T, E, K, "zipf", 1.1)
+    wts = wl.softmax_weights(rng, T, K)
+    op = EpDispatchCombineOp(EpDispatchCombineConfig(T, H, K, E, R), DEV)
+    out, out_w, _, out_idx, _ = op.dispatch(bf16_dev(x), torch.from_numpy(wts).to(DEV), None,
+                                            torch.from_numpy(idx).to(DEV))
+    ref = oracle.dispatch(x, wts, idx, E, R)
+    eo, ro = op.get_offsets()
+    np.testing.assert_array_equal(eo.cpu().numpy(), ref["expert_off"], err_msg="expert_off")
+    np.testing.assert_array_equal(ro.cpu().numpy(), ref["rank_off"], err_msg="rank_off")
+    n = ref["n_valid"]
+    bad = out_idx.clone()
+    s = n // 2
+    k = int(ref["src_token_pos"][s]) % K
+    bad[s, k] = (bad[s, k] + 1) % E      # row s no longer names its own expert in entry k
+    other = out_idx.clone()
+    other[s, (k + 1) % K] = (other[s, (k + 1) % K] + 1) % E   # an entry the check does not own
+
+    assert op.device_error() == 0
+    op.combine(out, out_w, bad)           # debug off: indices are not read
+    assert op.device_error() == 0
+    op.set_debug(True)
+    for given, flag in ((out_idx, 0), (None, 0), (other, 0), (bad, 4)):
+        y, y_w = op.combine(out, out_w, given)
+        assert op.device_error() == flag
+        check_combine(y, y_w, ref["out"], ref, T, K)
+    y, y_w = op.combine_scatter(out, out_w, bad)
+    assert op.device_error() == 4
+    check_combine(y, y_w, ref["out"], ref, T, K)
+    op.set_debug(False)
+    op.combine(out, out_w, bad)
+    assert op.device_error() == 0
+    with pytest.raises(B.EpdcError) as ei:
+        B.epdc_set_debug(op._op, 2)
+    assert ei.value.status == B.EPDC_ERR_INVALID_ARGS
