@@ -44,7 +44,27 @@ def build(verbose: bool = False) -> str:
     if verbose and msg.strip():
         print(msg, file=sys.stderr)
     os.replace(tmp, LIB)
+    _write_build_info()
     return LIB
+
+
+def _write_build_info() -> None:
+    """Record the git revision the library was built at (build_info.json,
+    not tracked), so a run on a copy of the tree without .git can say it."""
+    import json
+    info = {"git": None, "dirty": None}
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"],
+                           capture_output=True, text=True, timeout=10)
+        if r.returncode == 0:
+            info["git"] = r.stdout.strip()
+            d = subprocess.run(["git", "-C", ROOT, "status", "--porcelain", "--untracked-files=no"],
+                               capture_output=True, text=True, timeout=10)
+            info["dirty"] = bool(d.stdout.strip()) if d.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    with open(os.path.join(PKG, "build_info.json"), "w") as fh:
+        json.dump(info, fh)
 
 
 def is_stale() -> bool:
