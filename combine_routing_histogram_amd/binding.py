@@ -46,6 +46,7 @@ EPDC_KERNEL_CHECK_INDICES = 11
 EPDC_NUM_KERNELS = 12
 
 EPDC_DEBUG_CHECK_INDICES = 1
+EPDC_STATIC_WORKSPACE_BYTES = 8 << 20
 
 
 class epdc_config(ctypes.Structure):
@@ -72,6 +73,7 @@ _SIGNATURES = {
     "epdc_workspace_bytes": (I32, [PCFG, ctypes.POINTER(SZ)]),
     "epdc_row_bytes": (I32, [PCFG, ctypes.POINTER(SZ), ctypes.POINTER(SZ)]),
     "epdc_create": (I32, [PCFG, P, SZ, ctypes.POINTER(P)]),
+    "epdc_create_static": (I32, [PCFG, ctypes.POINTER(P)]),
     "epdc_destroy": (I32, [P]),
     "epdc_dispatch": (I32, [P, P, I32, P, P, P, P, P, P, P, P, P]),
     "epdc_combine": (I32, [P, P, P, P, P, P, P]),
@@ -154,6 +156,12 @@ def epdc_row_bytes(cfg: epdc_config) -> Tuple[int, int]:
 def epdc_create(cfg: epdc_config, workspace: int, workspace_bytes: int) -> int:
     op = P(None)
     _check(lib().epdc_create(ctypes.byref(cfg), workspace, workspace_bytes, ctypes.byref(op)))
+    return op.value
+
+
+def epdc_create_static(cfg: epdc_config) -> int:
+    op = P(None)
+    _check(lib().epdc_create_static(ctypes.byref(cfg), ctypes.byref(op)))
     return op.value
 
 

@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -172,6 +173,37 @@ const char *const kKernelNames[EPDC_NUM_KERNELS] = {
     "k_combine", "k_units_to_experts", "k_experts_to_units", "k_combine_units",
     "k_combine_push", "k_combine_reduce", "k_check_indices"};
 
+// Workspace of the ops made by epdc_create_static, for callers that cannot
+// allocate device memory.  Each device the library runs on holds its own copy
+// for the life of the process.  In host code `scratch` names a host-side
+// stand-in, not device memory: the host only ever uses the per-device
+// address hipGetSymbolAddress returns for it (static_workspace below).
+constexpr size_t kStaticWorkspaceBytes = EPDC_STATIC_WORKSPACE_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kStaticWorkspaceBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on device `dev` (the current device), looked up
+// once per device.
+epdc_status static_workspace(int dev, void **ptr)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(EPDC_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(EPDC_ERR_GPU_OP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return EPDC_SUCCESS;
+}
+
 }  // namespace
 
 struct epdc_op {
@@ -185,6 +217,7 @@ struct epdc_op {
     bool units_routed;  // the last dispatch was rank-deduplicated
     int32_t last_tokens;
     int32_t debug;          // EPDC_DEBUG_* bits (epdc_set_debug)
+    bool static_ws;         // the workspace is the library's `scratch` (epdc_create_static)
     // split-phase completion markers (timing disabled), made on first use
     hipEvent_t ev_dispatch, ev_combine;
     bool dispatch_sent, combine_sent;
@@ -546,7 +579,7 @@ epdc_status epdc_row_bytes(const epdc_config *cfg, size_t *payload_bytes, size_t
 namespace {
 
 // Create an op on the current device over `workspace` (>= layout total bytes).
-epdc_status create_on(const epdc_config *cfg, void *workspace, epdc_op **op)
+epdc_status create_on(const epdc_config *cfg, void *workspace, bool static_ws, epdc_op **op)
 {
     const Layout lay = layout_for(*cfg);
     int dev = 0;
@@ -560,6 +593,11 @@ epdc_status create_on(const epdc_config *cfg, void *workspace, epdc_op **op)
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
         return fail(EPDC_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950",
                     dev, prop.gcnArchName);
+    if (static_ws) {
+        const epdc_status s = static_workspace(dev, &workspace);
+        if (s != EPDC_SUCCESS)
+            return s;
+    }
     // the sticky error flag and the other control words start at zero
     e = hipMemset(static_cast<uint8_t *>(workspace) + lay.ctrl, 0, sizeof(uint32_t) * kCtrlWords);
     if (e == hipSuccess)
@@ -586,6 +624,7 @@ epdc_status create_on(const epdc_config *cfg, void *workspace, epdc_op **op)
     o->units_routed = false;
     o->last_tokens = 0;
     o->debug = 0;
+    o->static_ws = static_ws;
     o->profiling = false;
     o->ev_cap = o->ev_used = 0;
     *op = o;
@@ -624,7 +663,24 @@ epdc_status epdc_create(const epdc_config *cfg, void *workspace, size_t workspac
     if (workspace_bytes < lay.total)
         return fail(EPDC_ERR_INVALID_ARGS, "workspace has %zu bytes, needs %zu", workspace_bytes,
                     lay.total);
-    return create_on(cfg, workspace, op);
+    return create_on(cfg, workspace, false, op);
+}
+
+epdc_status epdc_create_static(const epdc_config *cfg, epdc_op **op)
+{
+    epdc_status s = check_config(cfg);
+    if (s != EPDC_SUCCESS)
+        return s;
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    *op = nullptr;
+    const Layout lay = layout_for(*cfg);
+    if (lay.total > kStaticWorkspaceBytes)
+        return fail(EPDC_ERR_INVALID_ARGS,
+                    "this config needs %zu bytes of workspace; the library's static workspace "
+                    "holds %zu (use epdc_create with a caller workspace)",
+                    lay.total, kStaticWorkspaceBytes);
+    return create_on(cfg, nullptr, true, op);
 }
 
 epdc_status epdc_destroy(epdc_op *op)

@@ -180,6 +180,23 @@ def test_header_is_plain_c(tmp_path):
                     "-I", os.path.join(ROOT, "include"), str(src)], check=True)
 
 
+def test_static_create_rejects_configs_beyond_its_workspace(lib):
+    """epdc_create_static checks the workspace a config needs against the
+    library's static array before it touches any device."""
+    big = B.make_config(1 << 17, 7168, 8, 256, 8)      # 1M pairs: about 26 MiB
+    assert B.epdc_workspace_bytes(big) > B.EPDC_STATIC_WORKSPACE_BYTES
+    with pytest.raises(B.EpdcError) as ei:
+        B.epdc_create_static(big)
+    assert ei.value.status == B.EPDC_ERR_INVALID_ARGS
+    assert "static workspace" in str(ei.value)
+    with pytest.raises(B.EpdcError) as ei:
+        B.epdc_create_static(B.make_config(128, 100, 2, 8, 2))   # invalid config first
+    assert ei.value.status == B.EPDC_ERR_INVALID_ARGS
+    # every configuration the benchmarks use fits the static workspace
+    for name, w in wl.WORKLOADS.items():
+        assert B.epdc_workspace_bytes(_cfg(w)) <= B.EPDC_STATIC_WORKSPACE_BYTES, name
+
+
 def test_unit_conversion_rejects_undersized_tensors():
     """units_to_experts checks rows, widths and dtypes of caller tensors on the
     host: the kernel reads up to T * min(K, R) rows of each."""

@@ -1,0 +1,104 @@
+"""The op whose workspace is the library's static device array
+(epdc_create_static, for callers that cannot allocate device memory), called
+through the C ABI: every output of dispatch and combine must be identical to
+those of an op created over a caller workspace (epdc_create) on the same
+inputs, on two calls in a row, the second with fewer tokens, and the first
+also equal to the oracle's.
+"""
+import numpy as np
+import pytest
+import torch
+
+from combine_routing_histogram_amd import binding as B
+from combine_routing_histogram_amd import workloads as wl
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda", 0)
+QUANT = {"none": B.EPDC_QUANT_NONE, "fp8_e4m3_b128": B.EPDC_QUANT_FP8_E4M3_B128,
+         "mxfp4_b32": B.EPDC_QUANT_MXFP4_B32}
+
+
+class _Buffers:
+    """Caller-owned outputs of one op (capacity max_tokens * K rows)."""
+
+    def __init__(self, cfg, payload, scale, T_max, K, H):
+        n = T_max * K
+        self.out = torch.empty((n, payload), dtype=torch.uint8, device=DEV)
+        self.out_w = torch.empty((n, K), dtype=torch.float32, device=DEV)
+        self.out_s = torch.empty((n, max(scale, 4)), dtype=torch.uint8, device=DEV)
+        self.out_i = torch.empty((n, K), dtype=torch.int32, device=DEV)
+        self.recv = torch.empty(cfg.num_ranks, dtype=torch.int32, device=DEV)
+        self.y = torch.empty((T_max, H), dtype=torch.bfloat16, device=DEV)
+        self.y_w = torch.empty((T_max, K), dtype=torch.float32, device=DEV)
+
+    def clobber(self):
+        for t in (self.out, self.out_w, self.out_s, self.out_i, self.recv, self.y, self.y_w):
+            t.view(torch.uint8).fill_(0x5A)
+
+
+def _step(op, buf, quant, x, wts, idx, c_in, T):
+    st = torch.cuda.current_stream(DEV).cuda_stream
+    B.epdc_dispatch(op, st, T, x.data_ptr(), wts.data_ptr(), 0, idx.data_ptr(),
+                    buf.out.data_ptr(), buf.out_w.data_ptr(),
+                    buf.out_s.data_ptr() if quant else 0, buf.out_i.data_ptr(),
+                    buf.recv.data_ptr())
+    comb = buf.out if c_in is None else c_in
+    B.epdc_combine(op, st, comb.data_ptr(), buf.out_w.data_ptr(), buf.out_i.data_ptr(),
+                   buf.y.data_ptr(), buf.y_w.data_ptr())
+
+
+@pytest.mark.parametrize("name,t1,t2", [("deepseek_v3_bf16", 600, 100),
+                                        ("deepseek_v3_fp8", 300, 37)])
+def test_static_workspace_matches_caller_workspace(name, t1, t2):
+    w = wl.WORKLOADS[name]
+    print(f"no-alloc op {name} tokens {t1} then {t2}", flush=True)
+    quant = w.quant != "none"
+    cfg = B.make_config(t1, w.hidden, w.topk, w.experts, w.ranks, quant=QUANT[w.quant])
+    payload, scale = B.epdc_row_bytes(cfg)
+    ws_bytes = B.epdc_workspace_bytes(cfg)
+    assert ws_bytes <= B.EPDC_STATIC_WORKSPACE_BYTES
+    torch.cuda.set_device(DEV)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    op_ref = B.epdc_create(cfg, ws.data_ptr(), ws_bytes)
+    op_st = B.epdc_create_static(cfg)
+    try:
+        ref = _Buffers(cfg, payload, scale, t1, w.topk, w.hidden)
+        got = _Buffers(cfg, payload, scale, t1, w.topk, w.hidden)
+        for call, T in enumerate((t1, t2)):
+            inp = wl.make_inputs(w, tokens=T, with_combine_input=quant)
+            x = torch.from_numpy(inp["x"].view(np.int16)).view(torch.bfloat16).to(DEV)
+            idx = torch.from_numpy(inp["indices"]).to(DEV)
+            wts = torch.from_numpy(inp["weights"]).to(DEV)
+            c_in = None
+            if quant:
+                c_in = torch.from_numpy(inp["combine_input"].view(np.int16)).view(
+                    torch.bfloat16).to(DEV)
+            ref.clobber()
+            got.clobber()
+            _step(op_ref, ref, quant, x, wts, idx, c_in, T)
+            _step(op_st, got, quant, x, wts, idx, c_in, T)
+            torch.cuda.synchronize()
+            n = T * w.topk   # every id is valid: all T*K rows are written
+            assert int(got.recv.sum()) == n
+            pairs = [(got.recv, ref.recv), (got.out[:n], ref.out[:n]),
+                     (got.out_w[:n], ref.out_w[:n]), (got.out_i[:n], ref.out_i[:n]),
+                     (got.y[:T], ref.y[:T]), (got.y_w[:T], ref.y_w[:T])]
+            if quant:
+                pairs.append((got.out_s[:n, :scale], ref.out_s[:n, :scale]))
+            for i, (a, b) in enumerate(pairs):
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), \
+                    f"call {call} (T={T}): output {i} differs from the caller-workspace op"
+            # the static op's routing also matches the oracle's, bit for bit
+            ptr, cnt = B.epdc_get_dispatch_src_token_pos(op_st)
+            assert cnt == n
+            o = oracle.dispatch(inp["x"], inp["weights"], inp["indices"], w.experts, w.ranks,
+                                quant=w.quant)
+            assert np.array_equal(got.recv.cpu().numpy(), o["recv_count"])
+            assert np.array_equal(got.out[:n].cpu().numpy(),
+                                  o["out"].view(np.uint8).reshape(n, -1))
+            assert B.epdc_get_device_error(op_st, 0) == 0
+    finally:
+        B.epdc_destroy(op_st)
+        B.epdc_destroy(op_ref)
