@@ -86,8 +86,10 @@ def traffic(fetch_dir: str, write_dir: str, kernel: str, calib_bytes: int) -> di
     f = read_counters(fetch_dir, "FETCH_SIZE")
     w = read_counters(write_dir, "WRITE_SIZE")
     calib = next(p for p in CALIB_PATTERNS if any(p in k for k in f))
-    cf = statistics.median(_pick(f, calib)) * 1024.0   # KiB -> bytes
-    cw = statistics.median(_pick(w, calib)) * 1024.0
+    # the calibration copy is the largest launch of the copy kernel (the run
+    # also uploads its inputs with small copies)
+    cf = max(_pick(f, calib)) * 1024.0   # KiB -> bytes
+    cw = max(_pick(w, calib)) * 1024.0
     kf = statistics.median(_pick(f, kernel)) * 1024.0
     kw = statistics.median(_pick(w, kernel)) * 1024.0
     sf, sw = calib_bytes / cf, calib_bytes / cw
