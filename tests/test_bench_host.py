@@ -1,0 +1,56 @@
+"""Host-side pieces of bench.py (CPU): the algorithmic bytes per step for
+each workload equal the figures derived in the survey's measurement table
+(x read once, K row copies written, K rows read back, one row written, plus
+the per-pair arrays), and the CPU-baseline leg times both oracle builds and
+finds their outputs identical."""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from combine_routing_histogram_amd import workloads as wl  # noqa: E402
+
+
+@pytest.mark.parametrize("name,dispatch,combine", [
+    ("tiny_bf16", 204_800, 199_680),
+    ("deepseek_v3_bf16", 531_103_744, 528_875_520),
+    ("deepseek_v3_fp8", 303_562_752, 528_875_520),
+    ("decode_bf16", 16_596_992, 16_527_360),
+    ("qwen3_moe_mxfp4", 429_916_160, 1_209_532_416),
+])
+def test_step_bytes_match_the_derived_table(name, dispatch, combine):
+    w = wl.WORKLOADS[name]
+    sk = bench.scatter_kernel(w)
+    assert bench.alg_bytes(sk, w) == dispatch
+    assert bench.alg_bytes("k_combine", w) == combine
+    assert bench.step_alg_bytes(w, "pair", "gather", None) == dispatch + combine
+
+
+def test_step_bytes_closed_form():
+    """dispatch = 2TH + N(P+Q) + 8TK + 8NK + 8N and combine = 2NH + 2TH + 12N,
+    N = T*K, for each payload kind."""
+    for w in wl.WORKLOADS.values():
+        T, H, K = w.tokens, w.hidden, w.topk
+        N = T * K
+        X, P, Q = bench.row_sizes(w)
+        d = X * T + N * (P + Q) + 8 * T * K + 8 * N * K + 8 * N
+        c = 2 * N * H + 2 * T * H + 12 * N
+        assert bench.alg_bytes(bench.scatter_kernel(w), w) == d, w.name
+        assert bench.alg_bytes("k_combine", w) == c, w.name
+
+
+def test_cpu_baseline_legs():
+    w = wl.WORKLOADS["tiny_bf16"]
+    inp = wl.make_inputs(w)
+    base, expected = bench.cpu_baseline(w, inp, 3, "pair", "gather")
+    assert base["legs"][0]["cores"] == 1 and base["legs"][1]["cores"] >= 1
+    assert base["openmp_result_identical"] is True
+    assert base["value"] == base["legs"][-1]["value"] > 0
+    assert all(len(leg["times_s"]) == 3 for leg in base["legs"])
+    assert expected["rows"] == w.tokens * w.topk
+    assert set(expected) >= {"recv", "payload", "weights", "indices", "src_pos", "y", "y_w"}
