@@ -233,6 +233,28 @@ struct epdc_op {
 
 namespace {
 
+// The op over each device's `scratch` (epdc_create_static): one per device,
+// since all of them would share the one workspace; each create re-configures
+// it in place, so the handle always describes what the workspace holds.
+// Guarded by g_scratch_mu.
+epdc_op g_static_ops[kMaxDevices];
+
+// Release the events an op holds (timing and split-phase markers).
+void release_events(epdc_op *op)
+{
+    for (hipEvent_t ev : op->ev)
+        (void)hipEventDestroy(ev);
+    op->ev.clear();
+    op->ev_kernel.clear();
+    op->ev_cap = op->ev_used = 0;
+    op->profiling = false;
+    if (op->ev_dispatch)
+        (void)hipEventDestroy(op->ev_dispatch);
+    if (op->ev_combine)
+        (void)hipEventDestroy(op->ev_combine);
+    op->ev_dispatch = op->ev_combine = nullptr;
+}
+
 // Launch `f` on `st`, bracketed by timing events when profiling.
 template <typename F>
 epdc_status launch(epdc_op *op, hipStream_t st, int kernel_id, F &&f)
@@ -593,10 +615,12 @@ epdc_status create_on(const epdc_config *cfg, void *workspace, bool static_ws, e
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
         return fail(EPDC_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950",
                     dev, prop.gcnArchName);
+    std::unique_lock<std::mutex> lock(g_scratch_mu, std::defer_lock);
     if (static_ws) {
         const epdc_status s = static_workspace(dev, &workspace);
         if (s != EPDC_SUCCESS)
             return s;
+        lock.lock();  // after static_workspace, which takes the same mutex
     }
     // the sticky error flag and the other control words start at zero
     e = hipMemset(static_cast<uint8_t *>(workspace) + lay.ctrl, 0, sizeof(uint32_t) * kCtrlWords);
@@ -605,7 +629,13 @@ epdc_status create_on(const epdc_config *cfg, void *workspace, bool static_ws, e
     if (e != hipSuccess)
         return fail(EPDC_ERR_GPU_OP, "clearing control words: %s", hipGetErrorString(e));
 
-    epdc_op *o = new epdc_op();
+    epdc_op *o;
+    if (static_ws) {
+        o = &g_static_ops[dev];
+        release_events(o);
+    } else {
+        o = new epdc_op();
+    }
     o->cfg = *cfg;
     o->ev_dispatch = o->ev_combine = nullptr;
     o->dispatch_sent = o->combine_sent = false;
@@ -687,12 +717,15 @@ epdc_status epdc_destroy(epdc_op *op)
 {
     if (!op)
         return ok();
-    for (hipEvent_t ev : op->ev)
-        (void)hipEventDestroy(ev);
-    if (op->ev_dispatch)
-        (void)hipEventDestroy(op->ev_dispatch);
-    if (op->ev_combine)
-        (void)hipEventDestroy(op->ev_combine);
+    if (op->static_ws) {  // the device's static op: forget its state, keep the object
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        release_events(op);
+        op->routed = op->units_routed = false;
+        op->dispatch_sent = op->combine_sent = false;
+        op->last_tokens = 0;
+        return ok();
+    }
+    release_events(op);
     delete op;
     return ok();
 }

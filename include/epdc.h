@@ -149,21 +149,22 @@ epdc_status epdc_create(const epdc_config *cfg, void *workspace,
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph
- * capture, tight serving loops, harnesses that forbid hipMalloc): create an
- * op on the current device whose workspace is the library's own static
- * device array of 8 MiB (EPDC_STATIC_WORKSPACE_BYTES), one per device, held
- * until the process ends.  No workspace argument; no hipMalloc, hipFree or
- * other allocating call (the op's host-side struct is plain heap memory).
- * The first call on a device looks up that device's copy of the array.
- * EPDC_ERR_INVALID_ARGS when epdc_workspace_bytes(cfg) exceeds the array
- * (about 25 bytes per (token, k) pair: max_tokens*topk above roughly
- * 300,000); otherwise as epdc_create,
- * and every other entry point works on the op unchanged.
- * All ops created this way on one device share the one array: the routing a
- * dispatch records is overwritten by the next dispatch on any of them, and
- * calls on them that overlap (on any streams) race.  Use one such op per
- * device at a time, with ordered calls.  Creating one clears the array's
- * control words (the sticky error flag).
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the op of
+ * the current device whose workspace is the library's own static device
+ * array of 8 MiB (EPDC_STATIC_WORKSPACE_BYTES), one array and one op per
+ * device, both held until the process ends.  No workspace argument, and no
+ * allocation of any kind: the first call on a device looks up that device's
+ * copy of the array, and every call configures the device's op in place for
+ * `cfg` and returns it (the same handle each time).  EPDC_ERR_INVALID_ARGS
+ * when epdc_workspace_bytes(cfg) exceeds the array (about 25 bytes per
+ * (token, k) pair: max_tokens*topk above roughly 300,000); otherwise as
+ * epdc_create, and every other entry point works on the op unchanged.
+ * Because there is one workspace per device, a call re-configures the op for
+ * everyone holding the handle: the recorded routing and any unreceived send
+ * are forgotten and the control words (the sticky error flag) cleared.
+ * Calls on the op must be ordered (one stream or ordered streams);
+ * overlapping calls race.  epdc_destroy on it forgets its state and releases
+ * its timing events but keeps the op and the array.
  */
 #define EPDC_STATIC_WORKSPACE_BYTES (8u << 20)
 epdc_status epdc_create_static(const epdc_config *cfg, epdc_op **op);

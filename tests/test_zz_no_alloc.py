@@ -1,9 +1,9 @@
 """The op whose workspace is the library's static device array
-(epdc_create_static, for callers that cannot allocate device memory), called
-through the C ABI: every output of dispatch and combine must be identical to
-those of an op created over a caller workspace (epdc_create) on the same
-inputs, on two calls in a row, the second with fewer tokens, and the first
-also equal to the oracle's.
+(epdc_create_static, for callers that cannot allocate), called through the C
+ABI: every output of dispatch and combine must be identical to those of an
+op created over a caller workspace (epdc_create) on the same inputs, on two
+calls in a row, the second with fewer tokens, and each also equal to the
+oracle's.  Creating it again returns the same op, configured afresh.
 """
 import numpy as np
 import pytest
@@ -99,6 +99,12 @@ def test_static_workspace_matches_caller_workspace(name, t1, t2):
             assert np.array_equal(got.out[:n].cpu().numpy(),
                                   o["out"].view(np.uint8).reshape(n, -1))
             assert B.epdc_get_device_error(op_st, 0) == 0
+        # one op per device: a second create returns the same handle, configured
+        # afresh (no routing recorded), and works again
+        assert B.epdc_create_static(cfg) == op_st
+        with pytest.raises(B.EpdcError) as ei:
+            B.epdc_combine(op_st, 0, got.out.data_ptr(), 0, 0, got.y.data_ptr(), 0)
+        assert ei.value.status == B.EPDC_ERR_BAD_STATE
     finally:
         B.epdc_destroy(op_st)
         B.epdc_destroy(op_ref)
