@@ -262,3 +262,30 @@ def test_combine_indices_debug_check(T):
     with pytest.raises(B.EpdcError) as ei:
         B.epdc_set_debug(op._op, 2)
     assert ei.value.status == B.EPDC_ERR_INVALID_ARGS
+
+
+def test_indices_check_after_deduplicated_dispatch():
+    """The pair routing recorded by the rank-deduplicated dispatch is what the
+    check compares with: the expert-layout indices from the conversion pass,
+    a corrupted entry is flagged."""
+    log("indices check after dedup")
+    rng = np.random.default_rng(91)
+    T, H, K, E, R = 600, 256, 8, 64, 8
+    x = wl.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    idx = wl.draw_topk(rng, T, E, K, "zipf", 1.1)
+    wts = wl.softmax_weights(rng, T, K)
+    op = EpDispatchCombineOp(EpDispatchCombineConfig(T, H, K, E, R), DEV)
+    op.set_debug(True)
+    op.dispatch_dedup(bf16_dev(x), torch.from_numpy(wts).to(DEV), None,
+                      torch.from_numpy(idx).to(DEV))
+    e_out, e_w, _, e_i, _ = op.units_to_experts()
+    ref = oracle.dispatch(x, wts, idx, E, R)
+    y, y_w = op.combine(e_out, e_w, e_i)
+    assert op.device_error() == 0
+    check_combine(y, y_w, ref["out"], ref, T, K)
+    bad = e_i.clone()
+    s = 17
+    k = int(ref["src_token_pos"][s]) % K
+    bad[s, k] = (bad[s, k] + 1) % E
+    op.combine(e_out, e_w, bad)
+    assert op.device_error() == 4
