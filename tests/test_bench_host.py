@@ -1,8 +1,8 @@
 """Host-side pieces of bench.py (CPU): the algorithmic bytes per step for
-each workload equal the figures derived in the survey's measurement table
-(x read once, K row copies written, K rows read back, one row written, plus
-the per-pair arrays), and the CPU-baseline leg times both oracle builds and
-finds their outputs identical."""
+each workload equal the counts worked out by hand from what the method must
+move (x read once, K row copies written, K rows read back, one row written,
+plus the per-pair arrays), and the CPU-baseline leg times both oracle builds
+and finds their outputs identical."""
 import os
 import sys
 
@@ -23,7 +23,7 @@ from combine_routing_histogram_amd import workloads as wl  # noqa: E402
     ("decode_bf16", 16_596_992, 16_527_360),
     ("qwen3_moe_mxfp4", 429_916_160, 1_209_532_416),
 ])
-def test_step_bytes_match_the_derived_table(name, dispatch, combine):
+def test_step_bytes_match_the_hand_counts(name, dispatch, combine):
     w = wl.WORKLOADS[name]
     sk = bench.scatter_kernel(w)
     assert bench.alg_bytes(sk, w) == dispatch
