@@ -54,3 +54,13 @@ def test_cpu_baseline_legs():
     assert all(len(leg["times_s"]) == 3 for leg in base["legs"])
     assert expected["rows"] == w.tokens * w.topk
     assert set(expected) >= {"recv", "payload", "weights", "indices", "src_pos", "y", "y_w"}
+
+
+def test_more_than_one_gpu_is_refused():
+    """The library has no multi-GPU path: bench.py says so and exits 2 before
+    touching any device."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
