@@ -38,6 +38,13 @@ def bytes_of(t):
     return t.contiguous().view(torch.uint8).cpu().numpy()
 
 
+def u8rows(a):
+    """Host array as bytes, one row per leading index (also for zero rows)."""
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint8).reshape(a.shape[0], int(np.prod(a.shape[1:], dtype=np.int64)) *
+                                    a.itemsize)
+
+
 @functools.lru_cache(maxsize=2)
 def inputs_for(name, tokens=None):
     w = wl.WORKLOADS[name]
@@ -83,7 +90,7 @@ def run_case(x, weights, indices, E, R, quant="none", max_tokens=None, hidden=No
     np.testing.assert_array_equal(so.cpu().numpy(), ref["slot_of"], err_msg="slot_of")
     np.testing.assert_array_equal(op.get_dispatch_src_token_pos()[:n].cpu().numpy(),
                                   ref["src_token_pos"], err_msg="src_token_pos")
-    np.testing.assert_array_equal(bytes_of(out[:n]), ref["out"].view(np.uint8).reshape(n, -1),
+    np.testing.assert_array_equal(bytes_of(out[:n]), u8rows(ref["out"]),
                                   err_msg="payload")
     np.testing.assert_array_equal(out_idx[:n].cpu().numpy(), ref["out_indices"],
                                   err_msg="out_indices")
@@ -92,7 +99,7 @@ def run_case(x, weights, indices, E, R, quant="none", max_tokens=None, hidden=No
                                       ref["out_weights"].view(np.uint32), err_msg="out_weights")
     if ref["out_scales"] is not None:
         np.testing.assert_array_equal(bytes_of(out_sc[:n]),
-                                      ref["out_scales"].view(np.uint8).reshape(n, -1),
+                                      u8rows(ref["out_scales"]),
                                       err_msg="out_scales")
 
     # combine: identity expert (the dispatch output) for bf16, else the given rows
@@ -455,3 +462,26 @@ def test_mxfp4_one_wave_per_row(T, H, K):
                              np.where(rng.random((T, H)) < 0.01, 20.0, 1.0)).astype(np.float32))
     c_in = wl.f32_to_bf16_bits(rng.standard_normal((T * K, H)).astype(np.float32))
     run_case(x, wl.softmax_weights(rng, T, K), idx, E, R, quant="mxfp4_b32", combine_input=c_in)
+
+
+@pytest.mark.parametrize("T", [100, 700])   # 400 pairs: routed inline; 2800: three tiles
+def test_every_expert_id_invalid(T):
+    """No pair has a row: every rank receives 0, nothing is written, combine
+    gives +0 with weight 0 everywhere, and the device flag is raised."""
+    log(f"all ids invalid T={T}")
+    rng = np.random.default_rng(T + 5)
+    H, K, E, R = 128, 4, 16, 4
+    x = wl.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    idx = np.where(rng.random((T, K)) < 0.5, -1, E + 3).astype(np.int32)
+    wts = rng.random((T, K)).astype(np.float32)
+    op, ref = run_case(x, wts, idx, E, R)
+    assert ref["n_valid"] == 0 and ref["recv_count"].tolist() == [0] * R
+    # the deduplicated path sees no unit either
+    op.dispatch_dedup(bf16_dev(x), torch.from_numpy(wts).to(DEV), None,
+                      torch.from_numpy(idx).to(DEV))
+    uo, _, _ = op.get_unit_routing()
+    assert uo.cpu().tolist() == [0] * (R + 1)
+    y, y_w = op.combine_units(None, None)
+    torch.cuda.synchronize()
+    assert not bits16(y).any() and not y_w.cpu().numpy().any()
+    assert op.device_error() == 1
