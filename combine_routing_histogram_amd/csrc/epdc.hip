@@ -1403,7 +1403,7 @@ epdc_status epdc_profile_begin(epdc_op *op, int32_t max_launches)
         hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableSystemFence);
         if (e != hipSuccess) {
             op->profiling = false;
-            return fail(EPDC_ERR_GPU_OP, "hipEventCreate: %s", hipGetErrorString(e));
+            return fail(EPDC_ERR_GPU_OP, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
         }
     }
     op->ev_cap = max_launches;
