@@ -383,7 +383,7 @@ class Bench:
         if graph:
             self._capture()
 
-    # the two phases of a step; each returns what the check compares
+    # the two phases of a step; check() reads their results from the op's buffers
     def dispatch(self):
         if self.path == "dedup":
             self.op.dispatch_dedup(self.x, self.wts, self.sc, self.idx)
