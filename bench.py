@@ -377,6 +377,9 @@ class Bench:
             EpDispatchCombineConfig(w.tokens, w.hidden, w.topk, w.experts, w.ranks,
                                     quant=w.quant, raw_row_bytes=w.raw_row_bytes,
                                     scale_row_bytes=w.scale_row_bytes), dev)
+        # the combine of identity experts reads the rows the dispatch has just
+        # written: say so (only the cache policy of its output stores changes)
+        self.op.set_combine_hint(recent_input=self.identity)
         self.expected = None
         self.graph = None
         self._scratch = None
@@ -779,6 +782,7 @@ def main() -> int:
                              else "bf16 rows"),
                    "combine_input": "identity (dispatch output)" if w.combine_input == "identity"
                    else "independent N(0,1) bf16 rows",
+                   "combine_hint": "recent input" if w.combine_input == "identity" else "cold input",
                    "graph_mode": "hip graph replay" if args.graph else "eager",
                    "path": args.path, "combine": args.combine, "unit_rows": units,
                    "protocol": (f"{head['flush']}; hipEvents ({args.events}) around dispatch "

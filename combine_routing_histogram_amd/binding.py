@@ -46,6 +46,8 @@ EPDC_KERNEL_CHECK_INDICES = 11
 EPDC_NUM_KERNELS = 12
 
 EPDC_DEBUG_CHECK_INDICES = 1
+EPDC_COMBINE_INPUT_COLD = 0
+EPDC_COMBINE_INPUT_RECENT = 1
 EPDC_STATIC_WORKSPACE_BYTES = 8 << 20
 
 
@@ -86,6 +88,7 @@ _SIGNATURES = {
     "epdc_get_routing": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P)]),
     "epdc_get_offsets": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(P)]),
     "epdc_set_debug": (I32, [P, I32]),
+    "epdc_set_combine_hint": (I32, [P, I32]),
     "epdc_combine_scatter": (I32, [P, P, P, P, P, P, P, P]),
     "epdc_dispatch_dedup": (I32, [P, P, I32, P, P, P, P, P, P, P, P, P]),
     "epdc_get_unit_routing": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P)]),
@@ -234,6 +237,10 @@ def epdc_get_offsets(op: int) -> Tuple[int, int]:
 
 def epdc_set_debug(op: int, flags: int) -> None:
     _check(lib().epdc_set_debug(op, flags))
+
+
+def epdc_set_combine_hint(op: int, hint: int) -> None:
+    _check(lib().epdc_set_combine_hint(op, hint))
 
 
 def epdc_combine_scatter(op: int, stream: int, input: int, weights: int, indices: int,

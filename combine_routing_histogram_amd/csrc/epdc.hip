@@ -217,6 +217,7 @@ struct epdc_op {
     bool units_routed;  // the last dispatch was rank-deduplicated
     int32_t last_tokens;
     int32_t debug;          // EPDC_DEBUG_* bits (epdc_set_debug)
+    int32_t combine_hint;   // EPDC_COMBINE_INPUT_* (epdc_set_combine_hint)
     bool static_ws;         // the workspace is the library's `scratch` (epdc_create_static)
     // split-phase completion markers (timing disabled), made on first use
     hipEvent_t ev_dispatch, ev_combine;
@@ -654,6 +655,7 @@ epdc_status create_on(const epdc_config *cfg, void *workspace, bool static_ws, e
     o->units_routed = false;
     o->last_tokens = 0;
     o->debug = 0;
+    o->combine_hint = EPDC_COMBINE_INPUT_COLD;
     o->static_ws = static_ws;
     o->profiling = false;
     o->ev_cap = o->ev_used = 0;
@@ -1118,6 +1120,7 @@ epdc_status epdc_combine(epdc_op *op, void *stream, const void *input, const flo
     ca.output = static_cast<uint8_t *>(output);
     ca.out_weights = out_weights;
     ca.xcd_order = one_tile_xcd_order((int64_t)T * c.topk);
+    ca.recent_input = op->combine_hint == EPDC_COMBINE_INPUT_RECENT;
     s = launch_combine_mode<kCombinePairs>(op, static_cast<hipStream_t>(stream),
                                            EPDC_KERNEL_COMBINE, ca, T);
     return s == EPDC_SUCCESS ? ok() : s;
@@ -1347,6 +1350,16 @@ epdc_status epdc_set_debug(epdc_op *op, int32_t flags)
     if (flags & ~EPDC_DEBUG_CHECK_INDICES)
         return fail(EPDC_ERR_INVALID_ARGS, "unknown debug flags 0x%x", (unsigned)flags);
     op->debug = flags;
+    return ok();
+}
+
+epdc_status epdc_set_combine_hint(epdc_op *op, int32_t hint)
+{
+    if (!op)
+        return fail(EPDC_ERR_INVALID_ARGS, "op is NULL");
+    if (hint != EPDC_COMBINE_INPUT_COLD && hint != EPDC_COMBINE_INPUT_RECENT)
+        return fail(EPDC_ERR_INVALID_ARGS, "unknown combine hint %d", hint);
+    op->combine_hint = hint;
     return ok();
 }
 

@@ -1235,6 +1235,7 @@ struct CombineArgs {
     int32_t xcd_order;         // 1: (row, segment) items in XCD order (xcd_item)
     int32_t seg_vecs;          // vectors per row segment (<= kWave * CH)
     int32_t cached_stores;     // 1: ordinary output stores that stay in the L2
+    int32_t recent_input;      // 1: the input rows were just written (device-scope output stores)
     // (Large batches keep nontemporal output stores in every mode: for the
     // expert->unit conversion, whose output is 40% of its bytes, device-scope
     // stores made the deduplicated headline step 404 -> 409 us and ordinary
@@ -1452,14 +1453,17 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
     if (MODE == kCombinePairs && a.out_weights && sg == 0 && lane < n)
         a.out_weights[t * K + my_k] = my_w;
 
-    // Nontemporal output stores: ordinary stores of the output slow this
-    // read-dominated kernel down by 10-13% when its input rows come from HBM
-    // (measured on gfx950); they are 2-3% faster only when half the input is
-    // still in the MALL from the scatter that just wrote it.  Outputs that
-    // the next kernel reads from this XCD's L2 (cached_stores) take buffer
-    // stores with no policy bits: an ordinary global store in one branch and
-    // a nontemporal one in the other would be merged by the compiler into
-    // one store without the nontemporal hint.
+    // Nontemporal output stores by default: device-scope or ordinary stores
+    // of the output slow this read-dominated kernel down by 7-12% when its
+    // input rows come from HBM (measured on gfx950).  When the input rows were
+    // written just before (recent_input: the caller says so), part of them sit
+    // dirty in the MALL and are written back while the combine reads them;
+    // device-scope output stores are then 5-6% faster.  Outputs that the next
+    // kernel reads from this XCD's L2 (cached_stores) take buffer stores with
+    // no policy bits.  The cached variants are buffer stores because an
+    // ordinary global store in one branch and a nontemporal one in the other
+    // would be merged by the compiler into one store without the nontemporal
+    // hint.
     const __amdgpu_buffer_rsrc_t orow = row_rsrc(a.output, (size_t)V * 16, t);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
@@ -1469,6 +1473,8 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
         if (j < end) {
             if (a.cached_stores)
                 __builtin_amdgcn_raw_buffer_store_b128(v, orow, j * 16, 0, 0);
+            else if (a.recent_input)
+                __builtin_amdgcn_raw_buffer_store_b128(v, orow, j * 16, 0, kStoreDeviceScope);
             else
                 __builtin_nontemporal_store(v, out + j);
         }

@@ -517,6 +517,13 @@ class EpDispatchCombineOp:
         recorded routing and raises bit 4 of the device error flag on a mismatch."""
         B.epdc_set_debug(self._op, B.EPDC_DEBUG_CHECK_INDICES if check_indices else 0)
 
+    def set_combine_hint(self, recent_input: bool) -> None:
+        """Say whether combine's input rows were written just before it (the
+        expert output, or the dispatch output itself); only the output stores'
+        cache policy depends on it."""
+        B.epdc_set_combine_hint(self._op, B.EPDC_COMBINE_INPUT_RECENT if recent_input
+                                else B.EPDC_COMBINE_INPUT_COLD)
+
     def get_registered_combine_input_buffer(self, dtype=torch.bfloat16) -> torch.Tensor:
         """A capacity-sized [N_cap, H] buffer owned by the op, for expert outputs."""
         if dtype != torch.bfloat16:

@@ -123,6 +123,17 @@ enum {
     EPDC_NUM_KERNELS = 12
 };
 
+/* What the caller knows about combine's input rows (epdc_set_combine_hint):
+ * only the cache policy of the output stores depends on it, never a result. */
+enum {
+    /* default: the input was written long before (HBM-resident) */
+    EPDC_COMBINE_INPUT_COLD = 0,
+    /* the input rows were written just before the combine (by the expert
+     * computation, or the dispatch itself for identity experts), so part of
+     * them sits dirty in the last-level cache */
+    EPDC_COMBINE_INPUT_RECENT = 1
+};
+
 /* Debug switches (epdc_set_debug). */
 enum {
     /* combine and combine_scatter check a non-NULL `indices` against the
@@ -372,6 +383,15 @@ epdc_status epdc_get_offsets(epdc_op *op, const int32_t **expert_off,
  * pair p, -1 if none).  Any may be NULL.  BAD_STATE if none. */
 epdc_status epdc_get_routing(epdc_op *op, const int32_t **expert_off,
                              const int32_t **rank_off, const int32_t **slot_of);
+
+/* Tell epdc_combine how recently its input rows were written
+ * (EPDC_COMBINE_INPUT_*; COLD is the default).  A performance hint for the
+ * output stores' cache policy, measured on MI355X: with RECENT the combine's
+ * output takes device-scope stores, 5-6% faster when the input is still
+ * partly in the last-level cache and 7-12% slower when it is not; COLD keeps
+ * nontemporal stores.  Results are identical either way.  Host state only;
+ * INVALID_ARGS for an unknown value. */
+epdc_status epdc_set_combine_hint(epdc_op *op, int32_t hint);
 
 /* Switch debug checks on or off for this op (EPDC_DEBUG_* bits; 0 = none,
  * the default).  Host state only.  INVALID_ARGS for an unknown bit. */

@@ -154,6 +154,7 @@ def test_every_entry_point_rejects_a_null_op(lib):
         lambda: B.epdc_get_routing(0),
         lambda: B.epdc_get_offsets(0),
         lambda: B.epdc_set_debug(0, 1),
+        lambda: B.epdc_set_combine_hint(0, 1),
         lambda: B.epdc_get_dispatch_src_token_pos(0),
     ]
     for call in calls:

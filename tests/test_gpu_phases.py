@@ -289,3 +289,28 @@ def test_indices_check_after_deduplicated_dispatch():
     bad[s, k] = (bad[s, k] + 1) % E
     op.combine(e_out, e_w, bad)
     assert op.device_error() == 4
+
+
+@pytest.mark.parametrize("name,recent", [("deepseek_v3_bf16", True), ("deepseek_v3_fp8", True),
+                                         ("deepseek_v3_bf16", False)])
+def test_combine_hint_changes_no_result(name, recent):
+    """The combine-input hint only picks the output stores' cache policy: at
+    full size the combine stays bit-identical to the oracle either way."""
+    w = wl.WORKLOADS[name]
+    log(f"combine hint {name} recent={recent}")
+    inp = wl.make_inputs(w, with_combine_input=True)
+    op = EpDispatchCombineOp(EpDispatchCombineConfig(w.tokens, w.hidden, w.topk, w.experts,
+                                                     w.ranks, quant=w.quant), DEV)
+    op.set_combine_hint(recent)
+    out, out_w, _, out_idx, _ = op.dispatch(bf16_dev(inp["x"]),
+                                            torch.from_numpy(inp["weights"]).to(DEV), None,
+                                            torch.from_numpy(inp["indices"]).to(DEV))
+    ref = oracle.dispatch(inp["x"], inp["weights"], inp["indices"], w.experts, w.ranks,
+                          quant=w.quant)
+    identity = w.quant == "none"
+    c_in_host = ref["out"] if identity else inp["combine_input"]
+    y, y_w = op.combine(out if identity else bf16_dev(c_in_host), out_w, out_idx)
+    check_combine(y, y_w, c_in_host, ref, w.tokens, w.topk)
+    with pytest.raises(B.EpdcError) as ei:
+        B.epdc_set_combine_hint(op._op, 7)
+    assert ei.value.status == B.EPDC_ERR_INVALID_ARGS
