@@ -347,7 +347,8 @@ class Bench:
     """One workload on the GPU: op, resident inputs, expected outputs on the
     device, and the step / check / timing loops."""
 
-    def __init__(self, w, dev, path="pair", combine="gather", graph=False, events="nofence"):
+    def __init__(self, w, dev, path="pair", combine="gather", graph=False, events="nofence",
+                 combine_hint="auto"):
         import numpy as np
         import torch
 
@@ -378,8 +379,9 @@ class Bench:
                                     quant=w.quant, raw_row_bytes=w.raw_row_bytes,
                                     scale_row_bytes=w.scale_row_bytes), dev)
         # the combine of identity experts reads the rows the dispatch has just
-        # written: say so (only the cache policy of its output stores changes)
-        self.op.set_combine_hint(recent_input=self.identity)
+        # written: say so (only how its output is stored changes)
+        self.recent = self.identity if combine_hint == "auto" else combine_hint == "recent"
+        self.op.set_combine_hint(recent_input=self.recent)
         self.expected = None
         self.graph = None
         self._scratch = None
@@ -607,6 +609,9 @@ def main() -> int:
                          "conversion back and unit combine")
     ap.add_argument("--combine", choices=["gather", "scatter"], default="gather",
                     help="pair path only: gather combine (default) or scatter (push) combine")
+    ap.add_argument("--combine-hint", choices=["auto", "cold", "recent"], default="auto",
+                    help="what the op is told about combine's input: auto = recent when the "
+                         "combine reads the dispatch output (identity experts), else cold")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and replay it in the timed loops "
                          "(phases are then not timed separately)")
@@ -665,7 +670,8 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    b = Bench(w, dev, args.path, args.combine, graph=args.graph, events=args.events)
+    b = Bench(w, dev, args.path, args.combine, graph=args.graph, events=args.events,
+              combine_hint=args.combine_hint)
     cpu = None
     if check or args.cpu_reps > 0:
         t0 = time.perf_counter()
@@ -716,6 +722,7 @@ def main() -> int:
             ph = head["combine"]["mean_us"]
             roof["achieved_timed_phase"] = dk["alg_bytes"] / (ph * 1e-6) / 1e9
 
+    recent = b.recent
     b.op = None
     del b
     torch.cuda.empty_cache()
@@ -782,7 +789,7 @@ def main() -> int:
                              else "bf16 rows"),
                    "combine_input": "identity (dispatch output)" if w.combine_input == "identity"
                    else "independent N(0,1) bf16 rows",
-                   "combine_hint": "recent input" if w.combine_input == "identity" else "cold input",
+                   "combine_hint": "recent input" if recent else "cold input",
                    "graph_mode": "hip graph replay" if args.graph else "eager",
                    "path": args.path, "combine": args.combine, "unit_rows": units,
                    "protocol": (f"{head['flush']}; hipEvents ({args.events}) around dispatch "

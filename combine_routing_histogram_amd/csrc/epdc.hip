@@ -510,16 +510,25 @@ epdc_status launch_scatter(epdc_op *op, hipStream_t st, ScatterArgs &sa, int mod
 }
 
 template <int KT, int MODE>
-void launch_combine(int grid, int block, hipStream_t st, const CombineArgs &a)
+void launch_combine(int grid, int block, size_t lds, hipStream_t st, const CombineArgs &a)
 {
-    k_combine<KT, kCombineSeg, MODE><<<grid, block, 0, st>>>(a);
+    k_combine<KT, kCombineSeg, MODE><<<grid, block, lds, st>>>(a);
 }
+
+// A gather combine over at least this many bytes of cold input rows runs
+// with fewer waves per CU: its launch reserves LDS that the kernel does not
+// use (kCombineLdsReserve, so at most two 4-wave blocks share a CU's
+// 160 KiB).  Measured on gfx950 with top-8 bf16 rows: 1-2% faster at 0.75 GiB
+// of input, 3-4% at 1-1.3 GiB, 5-6% at 2 GiB; equal or up to 3% slower
+// below 0.5 GiB.
+constexpr int64_t kCombineFewWavesBytes = int64_t(768) << 20;
+constexpr size_t kCombineLdsReserve = size_t(64) << 10;
 
 // One wave per (row, 2 KiB segment) over `rows` output rows; with
 // local_seg_vecs > 0 the XCD-local layout (dedup_local_seg_vecs).
 template <int MODE>
 epdc_status launch_combine_mode(epdc_op *op, hipStream_t st, int kernel_id, CombineArgs &ca,
-                                int64_t rows, int local_seg_vecs = 0)
+                                int64_t rows, int local_seg_vecs = 0, size_t lds = 0)
 {
     const epdc_config &c = op->cfg;
     ca.topk = c.topk;
@@ -539,12 +548,64 @@ epdc_status launch_combine_mode(epdc_op *op, hipStream_t st, int kernel_id, Comb
     grid = blocks_for(rows * ca.segs, block / kWave, ca.xcd_order);
     return launch(op, st, kernel_id, [&] {
         switch (c.topk) {
-        case 1: launch_combine<1, MODE>(grid, block, st, ca); break;
-        case 2: launch_combine<2, MODE>(grid, block, st, ca); break;
-        case 4: launch_combine<4, MODE>(grid, block, st, ca); break;
-        case 6: launch_combine<6, MODE>(grid, block, st, ca); break;
-        case 8: launch_combine<8, MODE>(grid, block, st, ca); break;
-        default: launch_combine<0, MODE>(grid, block, st, ca); break;
+        case 1: launch_combine<1, MODE>(grid, block, lds, st, ca); break;
+        case 2: launch_combine<2, MODE>(grid, block, lds, st, ca); break;
+        case 4: launch_combine<4, MODE>(grid, block, lds, st, ca); break;
+        case 6: launch_combine<6, MODE>(grid, block, lds, st, ca); break;
+        case 8: launch_combine<8, MODE>(grid, block, lds, st, ca); break;
+        default: launch_combine<0, MODE>(grid, block, lds, st, ca); break;
+        }
+    });
+}
+
+// The staged gather combine (k_combine_staged): groups of up to four rows
+// per 8-wave block, 1 KiB segments, a row group of at most 64 KiB of LDS.
+constexpr int kCombineStageBytes = 64 << 10;
+constexpr int kCombineStageMaxRows = 4;
+constexpr int kCombineStageWaves = 8;
+constexpr int kCombineStageSeg = 1;
+
+template <int KT>
+void launch_combine_staged(int grid, int block, size_t lds, hipStream_t st, const CombineArgs &a)
+{
+    k_combine_staged<KT, kCombineStageSeg><<<grid, block, lds, st>>>(a);
+}
+
+// Rows per block for the staged combine, or 0 where the plain one runs: the
+// staged form takes large batches of cold input in rows whose byte size is
+// not a power of two (k_combine_staged).
+int combine_stage_rows(const epdc_config &c, const CombineArgs &ca)
+{
+    if (ca.recent_input || ca.xcd_order || ca.cached_stores)
+        return 0;
+    const int64_t row_bytes = (int64_t)(c.hidden / 8) * 16;
+    if (row_bytes > kCombineStageBytes || (row_bytes & (row_bytes - 1)) == 0)
+        return 0;
+    const int64_t g = kCombineStageBytes / row_bytes;
+    return (int)(g < kCombineStageMaxRows ? g : kCombineStageMaxRows);
+}
+
+epdc_status launch_combine_staged_mode(epdc_op *op, hipStream_t st, CombineArgs &ca, int64_t rows,
+                                       int stage_rows)
+{
+    const epdc_config &c = op->cfg;
+    ca.topk = c.topk;
+    ca.row_vecs = c.hidden / 8;
+    ca.seg_vecs = kWave * kCombineStageSeg;
+    ca.segs = (ca.row_vecs + ca.seg_vecs - 1) / ca.seg_vecs;
+    ca.num_tokens = (int32_t)rows;
+    ca.stage_rows = stage_rows;
+    const int grid = (int)((rows + stage_rows - 1) / stage_rows);
+    const int block = kCombineStageWaves * kWave;
+    const size_t lds = (size_t)stage_rows * ca.row_vecs * 16;
+    return launch(op, st, EPDC_KERNEL_COMBINE, [&] {
+        switch (c.topk) {
+        case 1: launch_combine_staged<1>(grid, block, lds, st, ca); break;
+        case 2: launch_combine_staged<2>(grid, block, lds, st, ca); break;
+        case 4: launch_combine_staged<4>(grid, block, lds, st, ca); break;
+        case 6: launch_combine_staged<6>(grid, block, lds, st, ca); break;
+        case 8: launch_combine_staged<8>(grid, block, lds, st, ca); break;
+        default: launch_combine_staged<0>(grid, block, lds, st, ca); break;
         }
     });
 }
@@ -1121,8 +1182,15 @@ epdc_status epdc_combine(epdc_op *op, void *stream, const void *input, const flo
     ca.out_weights = out_weights;
     ca.xcd_order = one_tile_xcd_order((int64_t)T * c.topk);
     ca.recent_input = op->combine_hint == EPDC_COMBINE_INPUT_RECENT;
-    s = launch_combine_mode<kCombinePairs>(op, static_cast<hipStream_t>(stream),
-                                           EPDC_KERNEL_COMBINE, ca, T);
+    const int stage_rows = combine_stage_rows(c, ca);
+    const bool few_waves = !ca.recent_input && !ca.xcd_order &&
+                           (int64_t)T * c.topk * c.hidden * 2 >= kCombineFewWavesBytes;
+    if (stage_rows > 0)
+        s = launch_combine_staged_mode(op, static_cast<hipStream_t>(stream), ca, T, stage_rows);
+    else
+        s = launch_combine_mode<kCombinePairs>(op, static_cast<hipStream_t>(stream),
+                                               EPDC_KERNEL_COMBINE, ca, T, 0,
+                                               few_waves ? kCombineLdsReserve : 0);
     return s == EPDC_SUCCESS ? ok() : s;
 }
 
