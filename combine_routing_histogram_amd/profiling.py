@@ -95,6 +95,7 @@ def traffic(fetch_dir: str, write_dir: str, kernel: str, calib_bytes: int) -> di
     sf, sw = calib_bytes / cf, calib_bytes / cw
     return {
         "kernel": kernel,
+        "launches_matched": sorted(k for k in f if kernel in k),
         "fetch_bytes_raw": kf, "write_bytes_raw": kw,
         "calibration_kernel": calib, "calibration_bytes": calib_bytes,
         "calibration_fetch_raw": cf, "calibration_write_raw": cw,
