@@ -98,8 +98,6 @@ def alg_bytes_units(kernel: str, w, units: int) -> int:
         return U * 2 * H + T * (4 * K + 2 * H + 8 * K)
     if kernel == "k_route_rank":
         return 8 * N * 2
-    if kernel == "k_route_scan":
-        return 0
     raise ValueError(kernel)
 
 
@@ -114,7 +112,8 @@ def alg_bytes(kernel: str, w) -> int:
       combine: read K rows (2KH) + slot_of and the K weights (8K); write
                the row (2H) and its K weights (4K)
       route:   read the indices (4K); write the in-tile ranks (4K); the scan
-               only touches the small tile table (counted as 0)
+               of its last block only touches the small tile table (counted
+               as 0)
     """
     T, H, K = w.tokens, w.hidden, w.topk
     X, P, Q = row_sizes(w)
@@ -132,7 +131,7 @@ def alg_bytes(kernel: str, w) -> int:
         per = 4 * K * H + 8 * K + 2 * H + 4 * K
     elif kernel == "k_route_rank":
         per = 8 * K
-    elif kernel in ("k_route_scan", "k_check_indices"):
+    elif kernel == "k_check_indices":
         return 0
     else:
         raise ValueError(kernel)

@@ -882,6 +882,9 @@ epdc_status dispatch_impl(epdc_op *op, void *stream, int32_t num_tokens, const v
     const int tiles_pad8 = (tiles + 7) & ~7;
     ra.tile_cnt16 = fused_scan ? reinterpret_cast<uint16_t *>(op->ws + op->lay.tile_cnt16) : nullptr;
     ra.tiles_pad8 = tiles_pad8;
+    // Otherwise, with several tiles, the last rank block to finish scans the
+    // table (k_route_rank, ticket_word): no second launch.
+    ra.ticket_word = !fused_scan && tiles > 1 ? kCtrlTicket0 : 0;
     if (dedup) {
         // the unit level: keys = destination ranks of the pairs that open a
         // unit; its offsets are both the expert and the rank offsets (one key
@@ -895,6 +898,7 @@ epdc_status dispatch_impl(epdc_op *op, void *stream, int32_t num_tokens, const v
         rb.expert_off = op->i32(op->lay.unit_off);
         rb.rank_off = op->i32(op->lay.unit_off);
         rb.recv_count = recv_count;
+        rb.ticket_word = tiles > 1 ? kCtrlTicket1 : 0;
         if (tiles == 1) {
             s = launch(op, st, EPDC_KERNEL_ROUTE, [&] {
                 k_route_rank2<true><<<dim3(1, 2), kRouteThreads, lds, st>>>(ra, rb);
@@ -903,10 +907,6 @@ epdc_status dispatch_impl(epdc_op *op, void *stream, int32_t num_tokens, const v
             s = launch(op, st, EPDC_KERNEL_ROUTE, [&] {
                 k_route_rank2<false><<<dim3(tiles, 2), kRouteThreads, lds, st>>>(ra, rb);
             });
-            if (s == EPDC_SUCCESS)
-                s = launch(op, st, EPDC_KERNEL_ROUTE_SCAN, [&] {
-                    k_route_scan2<<<dim3(1, 2), kRouteThreads, 0, st>>>(ra, rb);
-                });
         }
     } else {
         // One tile with tokens: the scatter launch below routes by itself.
@@ -925,9 +925,6 @@ epdc_status dispatch_impl(epdc_op *op, void *stream, int32_t num_tokens, const v
             s = launch(op, st, EPDC_KERNEL_ROUTE, [&] {
                 k_route_rank<false><<<tiles, kRouteThreads, lds, st>>>(ra);
             });
-            if (s == EPDC_SUCCESS)
-                s = launch(op, st, EPDC_KERNEL_ROUTE_SCAN,
-                           [&] { k_route_scan<<<1, kRouteThreads, 0, st>>>(ra); });
         }
     }
     if (s != EPDC_SUCCESS)

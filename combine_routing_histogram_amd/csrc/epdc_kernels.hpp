@@ -35,7 +35,7 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxTopk = 16;
 
 // Control words at the start of the workspace.
-enum { kCtrlError = 1, kCtrlWords = 64 };
+enum { kCtrlError = 1, kCtrlTicket0 = 2, kCtrlTicket1 = 3, kCtrlWords = 64 };
 
 // ---------------------------------------------------------------------------
 // Small wave helpers
@@ -78,17 +78,17 @@ __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0
 // ballots over the bits of the expert id (a match-any), the rank inside the
 // wave is the number of matching lower lanes, and the rank inside the tile
 // adds the counts of the same expert in lower waves.  The block writes the
-// tile's expert histogram as one row of a [tiles x experts] table.
-// k_route_scan (one block, next launch on the stream) turns the table into
-// expert_off = exclusive scan of the expert totals and, in place of each
-// count, the first slot of that expert's run inside that tile.  Slot of pair
-// p = table[tile(p)][e] + rank_in_tile[p]: experts ascending, pairs in
-// ascending p inside an expert.  With a single tile the rank kernel scans its
-// own histogram and the second launch is skipped; with a small table the
-// scatter blocks scan it themselves (kRouteTableScan below).  The kernel
-// boundary is the only cross-block synchronization: an in-kernel "last block
-// scans" scheme needs agent-scope fences, i.e. L2 writeback/invalidate across
-// the XCDs, and measured slower than the second launch.
+// tile's expert histogram as one row of a [tiles x experts] table, and the
+// last block to finish (route_scan_body) turns the table into expert_off =
+// exclusive scan of the expert totals and, in place of each count, the first
+// slot of that expert's run inside that tile.  Slot of pair p =
+// table[tile(p)][e] + rank_in_tile[p]: experts ascending, pairs in ascending
+// p inside an expert.  With a single tile the rank kernel scans its own
+// histogram; with a small table the scatter blocks scan it themselves
+// (kRouteTableScan below).  The last-block hand-off uses device-scope stores
+// and loads for the table rows and a device-scope ticket, not agent-scope
+// fences: those compile to an L2 writeback / invalidate across the XCDs and
+// made an earlier form of this scheme slower than a second launch.
 
 struct RouteArgs {
     const int32_t *indices;  // [n_pairs]
@@ -107,6 +107,7 @@ struct RouteArgs {
     int32_t *rank_off;       // [R+1]
     int32_t *recv_count;     // [R]
     uint32_t *ctrl;          // [kCtrlWords]
+    int32_t ticket_word;     // ctrl word counting finished rank blocks (table path, several tiles)
 };
 
 // LDS ints k_route_rank needs for E experts.
@@ -254,6 +255,8 @@ __device__ inline TileRank rank_tile(const int32_t *indices, int n_pairs, int E,
     return r;
 }
 
+__device__ inline void route_scan_body(const RouteArgs &a);
+
 template <bool SINGLE_TILE>
 __device__ inline void route_rank_body(const RouteArgs &a)
 {
@@ -282,8 +285,31 @@ __device__ inline void route_rank_body(const RouteArgs &a)
                     for (int b = a.tiles; b < a.tiles_pad8; ++b)
                         row[b] = 0;
             }
-        } else if (tid < E) {
-            a.tile_table[(size_t)tile * E + tid] = r.col_total;
+        } else {
+            // Last-block scan (ctrl[ticket_word] is the ticket).  The
+            // histogram row goes out with device-scope stores (visible to
+            // every XCD without an L2 writeback); each
+            // thread waits for its stores to complete before the block takes
+            // a ticket, so the block that draws the last ticket finds every
+            // row in place and reads them with device-scope loads.  No block
+            // waits for another.
+            if (tid < E)
+                __hip_atomic_store(&a.tile_table[(size_t)tile * E + tid], r.col_total,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            __shared__ int s_last;
+            if (tid == 0)
+                s_last = __hip_atomic_fetch_add(&a.ctrl[a.ticket_word], 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT) ==
+                         (uint32_t)(a.tiles - 1);
+            __syncthreads();
+            if (s_last) {
+                route_scan_body(a);
+                if (tid == 0)
+                    __hip_atomic_store(&a.ctrl[a.ticket_word], 0u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     } else {
         // the only tile: its histogram is the whole histogram
@@ -308,9 +334,17 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_rank2(RouteArgs a, Rout
     route_rank_body<SINGLE_TILE>(blockIdx.y == 0 ? a : b);
 }
 
-// One block.  Column chunks of up to kScanRegs tiles stay in registers
-// between the two passes; longer columns are re-read from memory.
+// The scan of the tile table by one block (the last rank block).  Column
+// chunks of up to kScanRegs tiles stay in registers between the two passes;
+// longer columns are re-read from memory.
 constexpr int kScanRegs = 16;
+
+// Table reads of the scan: device-scope loads, since the last rank block
+// reads rows other blocks wrote with device-scope stores during the launch.
+__device__ inline int32_t table_load(const int32_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ inline void route_scan_body(const RouteArgs &a)
 {
@@ -336,13 +370,13 @@ __device__ inline void route_scan_body(const RouteArgs &a)
         if (in_regs) {
 #pragma unroll
             for (int r = 0; r < kScanRegs; ++r)
-                vals[r] = (b0 + r < b1) ? a.tile_table[(size_t)(b0 + r) * E + col] : 0;
+                vals[r] = (b0 + r < b1) ? table_load(&a.tile_table[(size_t)(b0 + r) * E + col]) : 0;
 #pragma unroll
             for (int r = 0; r < kScanRegs; ++r)
                 sum += vals[r];
         } else {
             for (int b = b0; b < b1; ++b)
-                sum += a.tile_table[(size_t)b * E + col];
+                sum += table_load(&a.tile_table[(size_t)b * E + col]);
         }
         part[tid] = sum;
     }
@@ -373,7 +407,7 @@ __device__ inline void route_scan_body(const RouteArgs &a)
         } else {
             for (int b = b0; b < b1; ++b) {
                 const size_t i = (size_t)b * E + col;
-                const int c = a.tile_table[i];
+                const int c = table_load(&a.tile_table[i]);
                 a.tile_table[i] = run;
                 run += c;
             }
@@ -381,15 +415,6 @@ __device__ inline void route_scan_body(const RouteArgs &a)
     }
 }
 
-__global__ __launch_bounds__(kRouteThreads) void k_route_scan(RouteArgs a)
-{
-    route_scan_body(a);
-}
-
-__global__ __launch_bounds__(kRouteThreads) void k_route_scan2(RouteArgs a, RouteArgs b)
-{
-    route_scan_body(blockIdx.y == 0 ? a : b);
-}
 
 // ---------------------------------------------------------------------------
 // Dispatch scatter: one wave per (token, row segment)

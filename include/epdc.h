@@ -104,12 +104,14 @@ typedef struct epdc_op epdc_op;
 
 /* Kernel ids for the profiling calls below. */
 enum {
-    EPDC_KERNEL_ROUTE = 0,         /* per-tile histograms + stable in-tile ranks
-                                      (and the scan, when there is one tile; a
-                                      dispatch of at most 1024 pairs routes inside
-                                      its scatter launch instead, so it records
-                                      only the scatter kernel) */
-    EPDC_KERNEL_ROUTE_SCAN = 1,    /* scan to expert/rank offsets + tile bases */
+    EPDC_KERNEL_ROUTE = 0,         /* per-tile histograms + stable in-tile ranks,
+                                      and the scan to expert/rank offsets + tile
+                                      bases (by the last block to finish, or by
+                                      the scatter blocks for a small tile table;
+                                      a dispatch of at most 1024 pairs routes
+                                      inside its scatter launch instead, so it
+                                      records only the scatter kernel) */
+    EPDC_KERNEL_ROUTE_SCAN = 1,    /* reserved: the scan has no launch of its own */
     EPDC_KERNEL_SCATTER = 2,       /* slot + row copy (bf16 or raw) */
     EPDC_KERNEL_SCATTER_FP8 = 3,   /* slot + E4M3 quantize + copy */
     EPDC_KERNEL_SCATTER_MXFP4 = 4, /* slot + MXFP4 quantize + copy */
