@@ -158,3 +158,70 @@ def make_inputs(w: Workload, tokens: Optional[int] = None,
                                                           dtype=np.float32)
         out["combine_input"] = f32_to_bf16_bits(c)
     return out
+
+
+def fingerprint(inputs: Dict[str, np.ndarray]) -> Dict[str, dict]:
+    """Shape, dtype and SHA-256 of each drawn array (of its bytes, C order)."""
+    import hashlib
+    return {k: {"shape": list(v.shape), "dtype": str(v.dtype),
+                "sha256": hashlib.sha256(np.ascontiguousarray(v).tobytes()).hexdigest()}
+            for k, v in sorted(inputs.items())}
+
+
+def save_inputs(w: Workload, out_dir: str, tokens: Optional[int] = None) -> Dict[str, dict]:
+    """Write the inputs of ``w`` as .npy files (plain arrays, no pickles) and
+    a manifest.json with the workload and each array's fingerprint, so a run
+    can be repeated on exactly these inputs elsewhere.  Returns the manifest."""
+    import json
+    import os
+    os.makedirs(out_dir, exist_ok=True)
+    inputs = make_inputs(w, tokens=tokens)
+    for k, v in inputs.items():
+        np.save(os.path.join(out_dir, f"{k}.npy"), v, allow_pickle=False)
+    manifest = {"workload": dataclasses.asdict(w),
+                "tokens": w.tokens if tokens is None else int(tokens),
+                "arrays": fingerprint(inputs)}
+    with open(os.path.join(out_dir, "manifest.json"), "w") as fh:
+        json.dump(manifest, fh, indent=1)
+    return manifest
+
+
+def load_inputs(in_dir: str) -> Dict[str, np.ndarray]:
+    """Read arrays written by save_inputs, checking them against the manifest."""
+    import json
+    import os
+    with open(os.path.join(in_dir, "manifest.json")) as fh:
+        manifest = json.load(fh)
+    out = {k: np.load(os.path.join(in_dir, f"{k}.npy"), allow_pickle=False)
+           for k in manifest["arrays"]}
+    got = fingerprint(out)
+    if got != manifest["arrays"]:
+        bad = [k for k in got if got[k] != manifest["arrays"].get(k)]
+        raise ValueError(f"arrays do not match the manifest: {bad}")
+    return out
+
+
+def main(argv=None) -> int:
+    import argparse
+    import json
+    ap = argparse.ArgumentParser(description="Draw a workload's inputs and save them as .npy")
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("save")
+    s.add_argument("workload", choices=sorted(WORKLOADS))
+    s.add_argument("out_dir")
+    s.add_argument("--tokens", type=int, default=None)
+    f = sub.add_parser("fingerprint")
+    f.add_argument("workload", choices=sorted(WORKLOADS))
+    f.add_argument("--tokens", type=int, default=None)
+    a = ap.parse_args(argv)
+    w = WORKLOADS[a.workload]
+    if a.cmd == "save":
+        m = save_inputs(w, a.out_dir, a.tokens)
+    else:
+        m = fingerprint(make_inputs(w, tokens=a.tokens))
+    print(json.dumps(m, indent=1))
+    return 0
+
+
+if __name__ == "__main__":
+    raise SystemExit(main())
