@@ -290,6 +290,10 @@ def cpu_baseline(w, inp, reps: int, path: str, combine: str, builds=(False, True
 
 # ---- the GPU side ---------------------------------------------------------------------------
 
+# 512 MiB fills queued ahead of a back-to-back block of steps (about 70 us each)
+BACK_TO_BACK_GATE_FILLS = 16
+
+
 class HipEvent:
     """A HIP event of the process's HIP runtime (the one torch loaded),
     created with hipEventDisableSystemFence: recording it takes the
@@ -489,11 +493,22 @@ class Bench:
         torch = self.torch
         flush = self.make_flush(flush_mode)
         stream = torch.cuda.current_stream(self.dev)
+        back_to_back = flush_mode == "none"
+        if back_to_back:
+            # Back to back, a small step takes less GPU time than the host
+            # needs to launch it, and the events would time the host's launch
+            # rate.  So the warm-up and timed steps are queued behind about
+            # 1 ms of fills: the host has launched them all before the GPU
+            # reaches them, and the GPU sets the pace.  The fills only touch
+            # the scratch buffer; the warm-up steps run after them.
+            gate = self.make_flush("write")
+            for i in range(BACK_TO_BACK_GATE_FILLS):
+                gate(i)
         for i in range(warmup):
             flush(i)
             self.step()
-        torch.cuda.synchronize()
-        back_to_back = flush_mode == "none"
+        if not back_to_back:
+            torch.cuda.synchronize()
         events, mismatches = [], []
         for i in range(steps):
             flush(i)
@@ -529,6 +544,11 @@ class Bench:
         """Per-kernel HIP events (recorded by the library around each launch)."""
         torch = self.torch
         flush = self.make_flush(flush_mode)
+        if flush_mode == "none":
+            gate = self.make_flush("write")   # as in timed(): the GPU sets the pace
+            for i in range(BACK_TO_BACK_GATE_FILLS):
+                gate(i)
+            self.step()
         self.op.profile_begin(16 * steps)
         for i in range(steps):
             flush(i)
@@ -751,8 +771,16 @@ def main() -> int:
             if args.kernel_steps > 0:
                 r["kernels"] = kernel_table(eb.kernel_pass(args.kernel_steps, args.flush),
                                             ew, None)
+            # the same workload in the two other cache states (step figures only)
+            if args.clean_steps > 0:
+                r["clean_flush"] = measure(eb, args.clean_steps, args.warmup, "read", check, sb)
+            if args.warm_steps > 0:
+                r["warm"] = measure(eb, args.warm_steps, args.warmup, "none", check, sb)
             extras[name] = r
-            log(f"{name}: {r['ms_per_step'] * 1e3:.1f} us/step, parity {r['parity']}")
+            log(f"{name}: {r['ms_per_step'] * 1e3:.1f} us/step, parity {r['parity']}"
+                + (f"; clean flush {r['clean_flush']['ms_per_step'] * 1e3:.1f}"
+                   if "clean_flush" in r else "")
+                + (f"; warm {r['warm']['ms_per_step'] * 1e3:.1f}" if "warm" in r else ""))
             eb.op = None
             del eb
             torch.cuda.empty_cache()

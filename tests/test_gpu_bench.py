@@ -46,6 +46,8 @@ def test_default_line():
     for name, r in d["workloads"].items():
         assert r["parity"] == "bit-exact on all 3 timed steps", name
         assert r["ms_per_step"] > 0 and r["kernels"], name
+        assert r["clean_flush"]["parity"] == "bit-exact on all 3 timed steps", name
+        assert r["warm"]["parity"].startswith("bit-exact"), name
 
 
 @pytest.mark.parametrize("args", [("--path", "dedup"), ("--combine", "scatter"),
