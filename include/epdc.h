@@ -126,7 +126,7 @@ enum {
 };
 
 /* What the caller knows about combine's input rows (epdc_set_combine_hint):
- * only the cache policy of the output stores depends on it, never a result. */
+ * only how epdc_combine launches and stores depends on it, never a result. */
 enum {
     /* default: the input was written long before (HBM-resident) */
     EPDC_COMBINE_INPUT_COLD = 0,
@@ -387,12 +387,15 @@ epdc_status epdc_get_routing(epdc_op *op, const int32_t **expert_off,
                              const int32_t **rank_off, const int32_t **slot_of);
 
 /* Tell epdc_combine how recently its input rows were written
- * (EPDC_COMBINE_INPUT_*; COLD is the default).  A performance hint for the
- * output stores' cache policy, measured on MI355X: with RECENT the combine's
- * output takes device-scope stores, 5-6% faster when the input is still
- * partly in the last-level cache and 7-12% slower when it is not; COLD keeps
- * nontemporal stores.  Results are identical either way.  Host state only;
- * INVALID_ARGS for an unknown value. */
+ * (EPDC_COMBINE_INPUT_*; COLD is the default).  A performance hint, measured
+ * on MI355X: with RECENT the combine's output takes device-scope stores,
+ * 5-6% faster when the input is still partly in the last-level cache and
+ * 7-12% slower when it is not.  With COLD, batches of more than 1024 pairs
+ * use nontemporal stores and, for rows whose byte size is not a power of
+ * two, a form that writes groups of up to four output rows at once (6-7%
+ * faster at hidden 7168), else fewer waves per CU once the input rows span
+ * 768 MiB or more (3-6% faster).  Results are identical in every case.  Host
+ * state only; INVALID_ARGS for an unknown value. */
 epdc_status epdc_set_combine_hint(epdc_op *op, int32_t hint);
 
 /* Switch debug checks on or off for this op (EPDC_DEBUG_* bits; 0 = none,
