@@ -519,8 +519,9 @@ class EpDispatchCombineOp:
 
     def set_combine_hint(self, recent_input: bool) -> None:
         """Say whether combine's input rows were written just before it (the
-        expert output, or the dispatch output itself); only the output stores'
-        cache policy depends on it."""
+        expert output, or the dispatch output itself); only how the combine
+        launches and stores depends on it (epdc_set_combine_hint), never its
+        result."""
         B.epdc_set_combine_hint(self._op, B.EPDC_COMBINE_INPUT_RECENT if recent_input
                                 else B.EPDC_COMBINE_INPUT_COLD)
 
