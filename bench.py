@@ -601,6 +601,55 @@ def measure(bench: Bench, steps: int, warmup: int, flush_mode: str, check: bool,
                 f"{', '.join(bad[0][1])}")}
 
 
+def layers_measure(benches, steps: int, warmup: int, check: bool, step_bytes: int) -> dict:
+    """Several independent layers (each its own inputs, op and buffers) stepped
+    in turn with no flush: every layer's inputs have been pushed out of the
+    caches by the other layers' traffic, and the caches hold the previous
+    layer's data, as in a model that runs its MoE layers one after another.
+    Per-layer step = dispatch + combine by HIP events; the median over all
+    layer steps.  Each layer's last step is checked against the oracle."""
+    torch = benches[0].torch
+    stream = torch.cuda.current_stream(benches[0].dev)
+    gate = benches[0].make_flush("write")     # as in Bench.timed: the GPU sets the pace
+    for i in range(BACK_TO_BACK_GATE_FILLS):
+        gate(i)
+    for _ in range(warmup):
+        for b in benches:
+            b.step()
+    events = []
+    for _ in range(steps):
+        for b in benches:
+            e = [b.new_event() for _ in range(3)]
+            e[0].record(stream)
+            b.dispatch()
+            e[1].record(stream)
+            b.combine()
+            e[2].record(stream)
+            events.append(e)
+    torch.cuda.synchronize()
+    bad = []
+    if check:
+        for li, b in enumerate(benches):
+            m = b.check()
+            if m:
+                bad.append((li, m))
+    td = [e[0].elapsed_time(e[1]) for e in events]
+    tc = [e[1].elapsed_time(e[2]) for e in events]
+    per_step = [a + c for a, c in zip(td, tc)]
+    med = statistics.median(per_step)
+    tokens = benches[0].w.tokens
+    return {"layers": len(benches), "steps": steps, "warmup": warmup,
+            "flush": "none (layers in turn, each with its own inputs and buffers)",
+            "ms_per_step": med, "ms_per_step_mean": statistics.fmean(per_step),
+            "tokens_per_s": tokens / (med * 1e-3),
+            "step_gbps": step_bytes / (med * 1e-3) / 1e9,
+            "step_frac_of_hbm_peak": step_bytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "dispatch": summary(td), "combine": summary(tc),
+            "parity": None if not check else (
+                f"bit-exact on the last step of each of {len(benches)} layers" if not bad else
+                f"MISMATCH in layer {bad[0][0]}: {', '.join(bad[0][1])}")}
+
+
 def device_copy_gbps(torch, dev) -> float:
     a = torch.empty(FLUSH_BYTES // 2, dtype=torch.int16, device=dev)
     b = torch.empty_like(a)
@@ -645,6 +694,10 @@ def main() -> int:
                     help="steps of the secondary pass with a 512 MiB read before each (0 = skip)")
     ap.add_argument("--kernel-steps", type=int, default=20,
                     help="steps of the per-kernel event pass (0 = skip)")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="also step this many independent copies of the workload (own inputs, "
+                         "op and buffers) in turn with no flush, as a model's successive MoE "
+                         "layers (0 = skip)")
     ap.add_argument("--extras", choices=["default", "none"], default="default",
                     help="with the headline workload: also measure " + ", ".join(EXTRA_WORKLOADS))
     ap.add_argument("--extra-steps", type=int, default=20)
@@ -746,6 +799,27 @@ def main() -> int:
     del b
     torch.cuda.empty_cache()
 
+    layers = None
+    if args.layers > 0 and args.path == "pair" and args.combine == "gather" and not args.graph:
+        import dataclasses
+        lbs = []
+        for li in range(args.layers):
+            # each layer its own draw (another seed) and its own op and buffers
+            lw = dataclasses.replace(w, seed=w.seed + 7919 * (li + 1))
+            lb = Bench(lw, dev, events=args.events, combine_hint=args.combine_hint)
+            if check:
+                _, ref = cpu_baseline(lw, lb.inp, 1, "pair", "gather", builds=(True,))
+                lb.set_expected(ref)
+                del ref
+            lbs.append(lb)
+        layers = layers_measure(lbs, args.steps, args.warmup, check, step_bytes)
+        log(f"{args.layers} layers in turn: {layers['ms_per_step'] * 1e3:.1f} us/step, "
+            f"parity {layers['parity']}")
+        for lb in lbs:
+            lb.op = None
+        del lbs
+        torch.cuda.empty_cache()
+
     extras = None
     if args.extras == "default" and w.name == HEADLINE and args.path == "pair" \
             and args.combine == "gather" and not args.graph:
@@ -834,6 +908,7 @@ def main() -> int:
         "roofline": roof,
         "kernels": kernels,
         "warm": warm,
+        "layers": layers,
         "clean_flush": clean,
         "device_copy": None if copy_gbps is None else {
             "kernel": "512 MiB device-to-device copy (torch copy_), for reference",

@@ -25,7 +25,7 @@ def run_bench(*args, timeout=300):
 
 def test_default_line():
     d = run_bench("--steps", "4", "--warmup", "1", "--warm-steps", "3", "--clean-steps", "3",
-                  "--kernel-steps", "3", "--extra-steps", "3", "--cpu-reps", "1")
+                  "--kernel-steps", "3", "--extra-steps", "3", "--cpu-reps", "1", "--layers", "2")
     assert d["metric"].startswith("dispatch+combine tokens/s and achieved HBM GB/s")
     assert d["unit"] == "tokens/s" and d["value"] > 0 and d["ms_per_step"] > 0
     assert d["n_gpus"] == 1 and d["higher_is_better"] is True and d["dtype"] == "bf16"
@@ -34,6 +34,8 @@ def test_default_line():
     assert d["parity"] == "bit-exact on all 4 timed steps"
     assert d["warm"]["parity"].startswith("bit-exact") and d["clean_flush"]["parity"].startswith(
         "bit-exact")
+    assert d["layers"]["layers"] == 2 and d["layers"]["parity"] == (
+        "bit-exact on the last step of each of 2 layers")
     roof = d["roofline"]
     assert roof["bound"] == "hbm" and roof["peak"] == 8000.0 and roof["unit"] == "GB/s"
     assert 0 < roof["frac"] < 1 and abs(roof["achieved"] / roof["peak"] - roof["frac"]) < 1e-9
