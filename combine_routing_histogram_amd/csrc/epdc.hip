@@ -860,11 +860,13 @@ epdc_status dispatch_impl(epdc_op *op, void *stream, int32_t num_tokens, const v
     const size_t lds = sizeof(int32_t) * (size_t)route_lds_ints(c.num_experts);
     epdc_status s = EPDC_SUCCESS;
     bool inline_route = false;
-    // A small tile table is scanned by every scatter block instead of a scan
-    // launch, while all blocks together read at most kFusedScanMaxReads
-    // entries: 32 tiles x 256 experts over the 1024 blocks of the bf16 copy
-    // at 4096 tokens saves about 2 us per dispatch, the same table over the
-    // 7168 blocks of the FP8 scatter costs 9-23 us.
+    // A small tile table is scanned by every scatter block instead of by the
+    // last rank block, while all blocks together read at most
+    // kFusedScanMaxReads entries: for 32 tiles x 256 experts over the 1024
+    // blocks of the bf16 copy at 4096 tokens the dispatch phase measured
+    // 109.5 us against 112.5-112.9 us with the last-block scan; the same
+    // table over the 7168 blocks of the FP8 scatter cost 9-23 us more than
+    // a separate scan launch.
     bool fused_scan = false;
     if (!dedup && tiles > 1 && tiles <= 8 * kScanMaxLoads &&
         (int64_t)tiles * c.num_experts <= kFusedScanMaxEntries) {

@@ -708,7 +708,7 @@ enum {
     kRouteUnits = 3,        // rank-deduplicated: one row per (token, rank), from the unit table
     kRouteConvert = 4,      // a wave per unit row: its pairs' expert rows (standard-MoE layout)
     kRouteUnitsReplay = 5,  // unit rows of a rank-deduplicated dispatch recorded earlier
-    kRouteTableScan = 6     // tile histograms scanned by each block (no scan launch)
+    kRouteTableScan = 6     // tile histograms scanned by each block (not by the last rank block)
 };
 
 // ---- the scan folded into the scatter, for small tile tables ----
@@ -717,7 +717,7 @@ enum {
 // the (at most two) tiles its tokens fall in: expert totals summed over all
 // tiles, their exclusive scan, plus the counts of the earlier tiles.  Every
 // block reads the whole table, so the host uses this only while the table
-// is small; it saves the one-block scan launch.
+// is small; there it beats the scan by the last rank block.
 // Largest tile table (tiles x experts entries) the scatter blocks scan, and
 // the most table entries all blocks of one launch may read together.
 constexpr int kFusedScanMaxEntries = 8192;
