@@ -49,8 +49,12 @@ def _step(op, buf, quant, x, wts, idx, c_in, T):
                    buf.y.data_ptr(), buf.y_w.data_ptr())
 
 
+# 600 / 100 and 300 / 37 tokens: tile tables the scatter blocks scan; 3000 /
+# 2400 FP8 tokens: larger tables, scanned by the last rank block, whose ticket
+# lives in the static workspace's control words
 @pytest.mark.parametrize("name,t1,t2", [("deepseek_v3_bf16", 600, 100),
-                                        ("deepseek_v3_fp8", 300, 37)])
+                                        ("deepseek_v3_fp8", 300, 37),
+                                        ("deepseek_v3_fp8", 3000, 2400)])
 def test_static_workspace_matches_caller_workspace(name, t1, t2):
     w = wl.WORKLOADS[name]
     print(f"no-alloc op {name} tokens {t1} then {t2}", flush=True)
