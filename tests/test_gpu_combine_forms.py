@@ -32,10 +32,10 @@ def bf16_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
 
 
-def combine_both_hints(T, H, K, E, R, seed, invalid=0, independent=True):
+def combine_both_hints(T, H, K, E, R, seed, invalid=0, independent=True, weighted=True):
     """Dispatch once, then combine with each hint; both must equal the oracle."""
     print(f"combine forms T={T} H={H} K={K} E={E} R={R} invalid={invalid} "
-          f"independent={independent}", flush=True)
+          f"independent={independent} weighted={weighted}", flush=True)
     rng = np.random.default_rng(seed)
     x = wl.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
     idx = wl.draw_topk(rng, T, E, K, "zipf", 1.1)
@@ -51,10 +51,11 @@ def combine_both_hints(T, H, K, E, R, seed, invalid=0, independent=True):
         c_in = bf16_dev(c_host)
     else:
         c_host, c_in = ref["out"], out
-    ry, ry_w = oracle.combine(c_host, ref["out_weights"], ref["slot_of"], T, K)
+    ry, ry_w = oracle.combine(c_host, ref["out_weights"] if weighted else None, ref["slot_of"],
+                              T, K)
     for recent in (False, True):
         op.set_combine_hint(recent_input=recent)
-        y, y_w = op.combine(c_in, out_w, out_idx)
+        y, y_w = op.combine(c_in, out_w if weighted else None, out_idx)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(bits16(y), ry, err_msg=f"combine (recent={recent})")
         np.testing.assert_array_equal(y_w.cpu().numpy().view(np.uint32), ry_w.view(np.uint32),
@@ -78,6 +79,10 @@ def test_staged_combine_matches_oracle(T, H, K, E, R):
 def test_staged_combine_with_missing_pairs():
     ref = combine_both_hints(777, 7168, 8, 256, 8, seed=5, invalid=9)
     assert ref["invalid"] == 9
+
+
+def test_staged_combine_unweighted():
+    combine_both_hints(700, 7168, 8, 256, 8, seed=9, weighted=False)
 
 
 def test_staged_combine_of_the_dispatch_output():
