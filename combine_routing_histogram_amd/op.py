@@ -12,6 +12,7 @@ only the first sum(recv_count) rows are written by a dispatch.
 from __future__ import annotations
 
 import dataclasses
+import enum
 from typing import Optional, Tuple
 
 import torch
@@ -20,6 +21,19 @@ from . import binding as B
 
 QUANT = {"none": B.EPDC_QUANT_NONE, "fp8_e4m3_b128": B.EPDC_QUANT_FP8_E4M3_B128,
          "mxfp4_b32": B.EPDC_QUANT_MXFP4_B32}
+
+
+class EpDispatchCombineKernelType(enum.IntEnum):
+    """The kernel types of the MORI-EP section ("Communication APIs" page,
+    kernel types table), kept with their values so that code written against
+    that enum imports unchanged.  On one GPU the destination ranks are
+    segments of one HBM buffer, which is the intra-node case; the others move
+    data across nodes or through SDMA queues and are not built here."""
+    IntraNode = 0
+    InterNode = 1
+    InterNodeV1 = 2
+    InterNodeV1LL = 3
+    AsyncLL = 4
 
 
 @dataclasses.dataclass
@@ -32,6 +46,16 @@ class EpDispatchCombineConfig:
     quant: str = "none"            # "none", "fp8_e4m3_b128", "mxfp4_b32"
     raw_row_bytes: int = 0         # > 0: dispatch carries opaque byte rows
     scale_row_bytes: int = 0       # bytes of a carried per-token scale row
+    kernel_type: int = EpDispatchCombineKernelType.IntraNode
+
+    def __post_init__(self):
+        kt = EpDispatchCombineKernelType(self.kernel_type)   # ValueError for unknown values
+        if kt != EpDispatchCombineKernelType.IntraNode:
+            raise ValueError(f"kernel_type {kt.name} moves rows between nodes or through SDMA "
+                             "queues; on one GPU only IntraNode (rank segments of one HBM "
+                             "buffer) exists")
+        if self.quant not in QUANT:
+            raise ValueError(f"quant must be one of {sorted(QUANT)}")
 
     def to_c(self) -> B.epdc_config:
         kind = B.EPDC_IN_RAW if self.raw_row_bytes > 0 else B.EPDC_IN_BF16

@@ -225,3 +225,22 @@ def test_unit_conversion_rejects_undersized_tensors():
     for kw in bad:
         with pytest.raises(ValueError):
             op._check_unit_rows(**kw)
+
+
+def test_kernel_type_enum_and_config_checks():
+    """The pages' kernel-type enum imports with its values; only the
+    intra-node type exists on one GPU, and the config says so on creation."""
+    from combine_routing_histogram_amd.op import (EpDispatchCombineConfig,
+                                                  EpDispatchCombineKernelType)
+    assert [(k.name, int(k)) for k in EpDispatchCombineKernelType] == [
+        ("IntraNode", 0), ("InterNode", 1), ("InterNodeV1", 2), ("InterNodeV1LL", 3),
+        ("AsyncLL", 4)]
+    cfg = EpDispatchCombineConfig(16, 256, 2, 8, 2)
+    assert cfg.kernel_type == EpDispatchCombineKernelType.IntraNode
+    for kt in (1, 2, 3, 4):
+        with pytest.raises(ValueError, match="IntraNode"):
+            EpDispatchCombineConfig(16, 256, 2, 8, 2, kernel_type=kt)
+    with pytest.raises(ValueError):
+        EpDispatchCombineConfig(16, 256, 2, 8, 2, kernel_type=7)
+    with pytest.raises(ValueError, match="quant"):
+        EpDispatchCombineConfig(16, 256, 2, 8, 2, quant="fp8")
