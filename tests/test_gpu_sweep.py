@@ -4,7 +4,13 @@ combine, the scatter combine, routing replay, and the rank-deduplicated
 dispatch with both conversions and the unit combine.  Shapes, payload kinds,
 routing skew, invalid ids, missing weights and ragged token counts are drawn
 per case, so tile and segment boundaries land in many different places.
+
+EPDC_SWEEP_CASES=N runs N seeds instead of 24; seeds from 24 on also draw,
+for about a third of the cases, 700-6000 tokens (many routing tiles, so the
+table is scanned by the last rank block).  All 424 seeds were run once.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -60,10 +66,16 @@ def draw_case(rng):
                 skew=float(rng.choice([0.0, 1.1, 1.5])))
 
 
-@pytest.mark.parametrize("seed", range(24))
+SWEEP_CASES = int(os.environ.get("EPDC_SWEEP_CASES", "24"))
+
+
+@pytest.mark.parametrize("seed", range(SWEEP_CASES))
 def test_random_configurations(seed):
     rng = np.random.default_rng(5000 + seed)
     c = draw_case(rng)
+    if seed >= 24 and rng.random() < 0.35:   # the extended sweep: larger batches too
+        c["T"] = int(rng.integers(700, 6000))
+        c["T_max"] = c["T"] + int(rng.integers(0, 50))
     print(f"sweep seed={seed} {c}", flush=True)
     T, H, K, E, R = c["T"], c["H"], c["K"], c["E"], c["R"]
     raw = c["quant"] == "raw"
