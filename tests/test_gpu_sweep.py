@@ -124,11 +124,16 @@ def test_random_configurations(seed):
     np.testing.assert_array_equal(op.get_dispatch_src_token_pos()[:n].cpu().numpy(),
                                   ref["src_token_pos"])
     ry, ry_w = oracle.combine(c_in, ref["out_weights"], ref["slot_of"], T, K)
-    for comb in (op.combine, op.combine_scatter):
+    # the gather combine under both input hints (each hint picks its own launch
+    # form and stores), then the scatter combine
+    for comb, recent in ((op.combine, False), (op.combine, True), (op.combine_scatter, False)):
+        op.set_combine_hint(recent_input=recent)
         y, y_w = comb(c_in_d, out_w, out_i)
         torch.cuda.synchronize()
-        same(y, ry, T, comb.__name__)
-        same(y_w, ry_w, T, comb.__name__ + " weights")
+        same(y, ry, T, f"{comb.__name__} (recent={recent})")
+        same(y_w, ry_w, T, f"{comb.__name__} weights (recent={recent})")
+        y.view(torch.uint8).fill_(0x5A)
+    op.set_combine_hint(recent_input=False)
 
     # routing replay with a new payload
     if raw:
