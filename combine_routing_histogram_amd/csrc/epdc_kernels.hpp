@@ -1260,7 +1260,7 @@ struct CombineArgs {
     int32_t xcd_order;         // 1: (row, segment) items in XCD order (xcd_item)
     int32_t seg_vecs;          // vectors per row segment (<= kWave * CH)
     int32_t cached_stores;     // 1: ordinary output stores that stay in the L2
-    int32_t recent_input;      // 1: the input rows were just written (device-scope output stores)
+    int32_t recent_input;      // 1: the input rows were just written (cache-allocating output stores)
     int32_t stage_rows;        // k_combine_staged: output rows per block
     // (Large batches keep nontemporal output stores in every mode: for the
     // expert->unit conversion, whose output is 40% of its bytes, device-scope
@@ -1484,12 +1484,12 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
     // input rows come from HBM (measured on gfx950).  When the input rows were
     // written just before (recent_input: the caller says so), part of them sit
     // dirty in the MALL and are written back while the combine reads them;
-    // device-scope output stores are then 5-6% faster.  Outputs that the next
-    // kernel reads from this XCD's L2 (cached_stores) take buffer stores with
-    // no policy bits.  The cached variants are buffer stores because an
-    // ordinary global store in one branch and a nontemporal one in the other
-    // would be merged by the compiler into one store without the nontemporal
-    // hint.
+    // stores that allocate in the caches are then faster: buffer stores with
+    // no policy bits by 6-7%, device-scope ones by 5-6%.  Outputs that the
+    // next kernel reads from this XCD's L2 (cached_stores) take the same
+    // stores.  They are buffer stores because an ordinary global store in
+    // one branch and a nontemporal one in the other would be merged by the
+    // compiler into one store without the nontemporal hint.
     const __amdgpu_buffer_rsrc_t orow = row_rsrc(a.output, (size_t)V * 16, t);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
@@ -1497,10 +1497,8 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a)
         const u32x4 v = {pack_bf16_rne(acc[i][0], acc[i][1]), pack_bf16_rne(acc[i][2], acc[i][3]),
                          pack_bf16_rne(acc[i][4], acc[i][5]), pack_bf16_rne(acc[i][6], acc[i][7])};
         if (j < end) {
-            if (a.cached_stores)
+            if (a.cached_stores || a.recent_input)
                 __builtin_amdgcn_raw_buffer_store_b128(v, orow, j * 16, 0, 0);
-            else if (a.recent_input)
-                __builtin_amdgcn_raw_buffer_store_b128(v, orow, j * 16, 0, kStoreDeviceScope);
             else
                 __builtin_nontemporal_store(v, out + j);
         }

@@ -388,9 +388,9 @@ epdc_status epdc_get_routing(epdc_op *op, const int32_t **expert_off,
 
 /* Tell epdc_combine how recently its input rows were written
  * (EPDC_COMBINE_INPUT_*; COLD is the default).  A performance hint, measured
- * on MI355X: with RECENT the combine's output takes device-scope stores,
- * 5-6% faster when the input is still partly in the last-level cache and
- * 7-12% slower when it is not.  With COLD, batches of more than 1024 pairs
+ * on MI355X: with RECENT the combine's output takes stores that allocate in
+ * the caches, 6-7% faster when the input is still partly in the last-level
+ * cache and 7-12% slower when it is not.  With COLD, batches of more than 1024 pairs
  * use nontemporal stores and, for rows whose byte size is not a power of
  * two, a form that writes groups of up to four output rows at once (6-7%
  * faster at hidden 7168), else fewer waves per CU once the input rows span
