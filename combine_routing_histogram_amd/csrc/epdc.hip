@@ -524,6 +524,14 @@ void launch_combine(int grid, int block, size_t lds, hipStream_t st, const Combi
 constexpr int64_t kCombineFewWavesBytes = int64_t(768) << 20;
 constexpr size_t kCombineLdsReserve = size_t(64) << 10;
 
+// A combine of rows written just before (the RECENT hint) in the plain CU
+// order keeps three 4-wave blocks per CU the same way.  At 4096 x 7168 top-8
+// after the scatter (five runs each, gfx950): the kernel 2 us faster with
+// the steps back to back (97.4-97.8 against 99.3-100.1 us), the step 1 us
+// faster after a 512 MiB read and with layers stepped in turn, equal after a
+// 512 MiB write.
+constexpr size_t kCombineRecentLdsReserve = size_t(48) << 10;
+
 // One wave per (row, 2 KiB segment) over `rows` output rows; with
 // local_seg_vecs > 0 the XCD-local layout (dedup_local_seg_vecs).
 template <int MODE>
@@ -1182,14 +1190,16 @@ epdc_status epdc_combine(epdc_op *op, void *stream, const void *input, const flo
     ca.xcd_order = one_tile_xcd_order((int64_t)T * c.topk);
     ca.recent_input = op->combine_hint == EPDC_COMBINE_INPUT_RECENT;
     const int stage_rows = combine_stage_rows(c, ca);
-    const bool few_waves = !ca.recent_input && !ca.xcd_order &&
-                           (int64_t)T * c.topk * c.hidden * 2 >= kCombineFewWavesBytes;
+    size_t lds_reserve = 0;  // unused LDS that caps the blocks per CU
+    if (!ca.xcd_order && ca.recent_input)
+        lds_reserve = kCombineRecentLdsReserve;
+    else if (!ca.xcd_order && (int64_t)T * c.topk * c.hidden * 2 >= kCombineFewWavesBytes)
+        lds_reserve = kCombineLdsReserve;
     if (stage_rows > 0)
         s = launch_combine_staged_mode(op, static_cast<hipStream_t>(stream), ca, T, stage_rows);
     else
         s = launch_combine_mode<kCombinePairs>(op, static_cast<hipStream_t>(stream),
-                                               EPDC_KERNEL_COMBINE, ca, T, 0,
-                                               few_waves ? kCombineLdsReserve : 0);
+                                               EPDC_KERNEL_COMBINE, ca, T, 0, lds_reserve);
     return s == EPDC_SUCCESS ? ok() : s;
 }
 

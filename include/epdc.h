@@ -390,12 +390,14 @@ epdc_status epdc_get_routing(epdc_op *op, const int32_t **expert_off,
  * (EPDC_COMBINE_INPUT_*; COLD is the default).  A performance hint, measured
  * on MI355X: with RECENT the combine's output takes stores that allocate in
  * the caches, 6-7% faster when the input is still partly in the last-level
- * cache and 7-12% slower when it is not.  With COLD, batches of more than 1024 pairs
- * use nontemporal stores and, for rows whose byte size is not a power of
- * two, a form that writes groups of up to four output rows at once (6-7%
- * faster at hidden 7168), else fewer waves per CU once the input rows span
- * 768 MiB or more (3-6% faster).  Results are identical in every case.  Host
- * state only; INVALID_ARGS for an unknown value. */
+ * cache and 7-12% slower when it is not, and batches of more than 1024
+ * pairs run with at most three 4-wave blocks per CU (up to 2% faster).  With
+ * COLD, batches of more than 1024 pairs use nontemporal stores and, for rows
+ * whose byte size is not a power of two, a form that writes groups of up to
+ * four output rows at once (6-7% faster at hidden 7168), else fewer waves per
+ * CU once the input rows span 768 MiB or more (3-6% faster).  Results are
+ * identical in every case.  Host state only; INVALID_ARGS for an unknown
+ * value. */
 epdc_status epdc_set_combine_hint(epdc_op *op, int32_t hint);
 
 /* Switch debug checks on or off for this op (EPDC_DEBUG_* bits; 0 = none,
