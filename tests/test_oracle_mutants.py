@@ -98,6 +98,39 @@ MUTANTS = {
         "continue;\n                float w = weights ? weights[(long)s * K] : 1.0f;", False),
     "combine_units_adds_a_unit_twice": (
         "            if (seen)\n                continue;\n", "", False),
+    "combine_units_weight_column_0": (
+        "unit_weights[(long)u * K + k]", "unit_weights[(long)u * K]", False),
+    "units_placed_in_descending_token_order": (
+        "    for (int t = 0; t < T; ++t) {\n        for (int r = 0; r < R; ++r)\n"
+        "            open[r] = -1;",
+        "    for (int t = T - 1; t >= 0; --t) {\n        for (int r = 0; r < R; ++r)\n"
+        "            open[r] = -1;", False),
+    "units_to_experts_skips_pair_0": (
+        "for (long p = 0; p < n_pairs; ++p) {\n        if (slot_of[p] < 0 || unit_of[p] < 0)",
+        "for (long p = 1; p < n_pairs; ++p) {\n        if (slot_of[p] < 0 || unit_of[p] < 0)",
+        False),
+    # more routing, quantization and format mistakes
+    "rank_off_end_short_by_last_expert": (
+        "rank_off[R] = expert_off[E];", "rank_off[R] = expert_off[E - 1];", False),
+    "fp8_amax_without_abs": (
+        "float a = fabsf(bf16_to_f32(xb[i]));\n                if (a > amax)\n"
+        "                    amax = a;\n            }\n            float s = 0.0f;",
+        "float a = bf16_to_f32(xb[i]);\n                if (a > amax)\n"
+        "                    amax = a;\n            }\n            float s = 0.0f;", False),
+    "mxfp4_amax_without_abs": (
+        "float a = fabsf(bf16_to_f32(xb[i]));\n                if (a > amax)\n"
+        "                    amax = a;\n            }\n            int e;",
+        "float a = bf16_to_f32(xb[i]);\n                if (a > amax)\n"
+        "                    amax = a;\n            }\n            int e;", False),
+    "e8m0_bias_128": ("(uint8_t)(e + 127)", "(uint8_t)(e + 128)", False),
+    "mxfp4_zero_block_exponent_0": ("if (amax == 0.0f) {\n                e = -127;",
+                                    "if (amax == 0.0f) {\n                e = 0;", False),
+    "e4m3_bias_8_as_in_fnuz": ("int e_field = (ex - 1) + 7;", "int e_field = (ex - 1) + 8;",
+                               False),
+    "e4m3_subnormal_spacing_halved": (
+        "q = ldexp(1.0, -9);                      /* subnormal spacing */",
+        "q = ldexp(1.0, -10);                     /* subnormal spacing */", False),
+    "e2m1_top_binade_spacing_1": ("(a < 4.0 ? 1.0 : 2.0)", "(a < 4.0 ? 1.0 : 1.0)", False),
 }
 
 
