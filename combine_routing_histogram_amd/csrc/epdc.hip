@@ -301,7 +301,7 @@ ScatterPlan make_plan(int ch, int row_vecs, int max_segs)
     return p;
 }
 
-// Measured on MI355X in the dispatch -> combine loop (see the design notes):
+// Measured on MI355X in the dispatch -> combine loop:
 // the bf16 copy streams best with one wave per token once there are enough
 // tokens to fill the chip; the quantizing kernels and small batches need more,
 // shorter waves per token to hide their per-wave latency.
@@ -525,11 +525,11 @@ constexpr int64_t kCombineFewWavesBytes = int64_t(768) << 20;
 constexpr size_t kCombineLdsReserve = size_t(64) << 10;
 
 // A combine of rows written just before (the RECENT hint) in the plain CU
-// order keeps three 4-wave blocks per CU the same way.  At 4096 x 7168 top-8
-// after the scatter (five runs each, gfx950): the kernel 2 us faster with
-// the steps back to back (97.4-97.8 against 99.3-100.1 us), the step 1 us
-// faster after a 512 MiB read and with layers stepped in turn, equal after a
-// 512 MiB write.
+// order reserves LDS the same way for at most three 4-wave blocks per CU.  At
+// 4096 x 7168 top-8 after the scatter (five runs each, gfx950): the kernel up
+// to 2 us faster with the steps back to back (97.4-97.8 against 97.6-100.1
+// us), the step 1 us faster after a 512 MiB read and with layers stepped in
+// turn, equal after a 512 MiB write.
 constexpr size_t kCombineRecentLdsReserve = size_t(48) << 10;
 
 // One wave per (row, 2 KiB segment) over `rows` output rows; with
@@ -874,7 +874,7 @@ epdc_status dispatch_impl(epdc_op *op, void *stream, int32_t num_tokens, const v
     // blocks of the bf16 copy at 4096 tokens the dispatch phase measured
     // 109.5 us against 112.5-112.9 us with the last-block scan; the same
     // table over the 7168 blocks of the FP8 scatter cost 9-23 us more than
-    // a separate scan launch.
+    // scanning it once.
     bool fused_scan = false;
     if (!dedup && tiles > 1 && tiles <= 8 * kScanMaxLoads &&
         (int64_t)tiles * c.num_experts <= kFusedScanMaxEntries) {
@@ -923,10 +923,6 @@ epdc_status dispatch_impl(epdc_op *op, void *stream, int32_t num_tokens, const v
         inline_route = tiles == 1 && num_tokens > 0;
         if (inline_route) {
             // no route launch
-        } else if (fused_scan) {
-            s = launch(op, st, EPDC_KERNEL_ROUTE, [&] {
-                k_route_rank<false><<<tiles, kRouteThreads, lds, st>>>(ra);
-            });
         } else if (tiles == 1) {
             s = launch(op, st, EPDC_KERNEL_ROUTE, [&] {
                 k_route_rank<true><<<1, kRouteThreads, lds, st>>>(ra);

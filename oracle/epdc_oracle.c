@@ -31,12 +31,12 @@
  *  - the rank-deduplicated dispatch and the standard-MoE conversion: see the
  *    section of that name below.
  *
- * Readings where the pages are silent are listed in the design notes; the ones
- * that shape this file: an expert index outside [0,E) gives its pair no row
- * (slot -1) and is counted; an all-zero FP8 block has scale 0 and codes 0x00;
- * the MXFP4 shared exponent is floor(log2(amax)) - 2 clamped to [-127,127]
- * (-127 for amax == 0); combine accumulates k = 0..K-1 with a separate fp32
- * multiply and add, starting from +0.0f, then rounds to bf16 to nearest even.
+ * Where the pages are silent this file takes these readings: an expert
+ * index outside [0,E) gives its pair no row (slot -1) and is counted; an
+ * all-zero FP8 block has scale 0 and codes 0x00; the MXFP4 shared exponent is
+ * floor(log2(amax)) - 2 clamped to [-127,127] (-127 for amax == 0); combine
+ * accumulates k = 0..K-1 with a separate fp32 multiply and add, starting from
+ * +0.0f, then rounds to bf16 to nearest even.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -shared -fPIC (no fast-math).
  * A second build of the same source adds -fopenmp: the loops over tokens
