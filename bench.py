@@ -26,7 +26,9 @@ events in a further pass under the headline protocol), `workloads` (the
 FP8, MXFP4, decode and pre-quantized-FP8 workloads under the headline
 protocol, each with parity on every timed step), `cpu_baseline` (the oracle,
 plain C, on one thread and with OpenMP over tokens on all host cores,
-median of 3 whole steps each).
+median of 3 whole steps each), `ceilings` (HBM read, write and copy rates of
+streaming probe kernels over 4 GiB, and each kernel's read and written bytes
+priced at those rates against its measured time).
 
 roofline: the kernel with the most time in the per-kernel pass; algorithmic
 bytes per launch / its mean event duration, against 8000 GB/s.
@@ -136,6 +138,20 @@ def alg_bytes(kernel: str, w) -> int:
     else:
         raise ValueError(kernel)
     return per * T
+
+
+def alg_read_write(kernel: str, w):
+    """alg_bytes(kernel, w) split into (bytes read, bytes written), for the
+    pair path's launches (route, scatter, gather combine)."""
+    T, H, K = w.tokens, w.hidden, w.topk
+    X, P, Q = row_sizes(w)
+    if kernel.startswith("k_scatter"):
+        return T * (X + 8 * K), T * (K * (P + Q) + 8 * K * K + 8 * K)
+    if kernel == "k_combine":
+        return T * (2 * K * H + 8 * K), T * (2 * H + 4 * K)
+    if kernel == "k_route_rank":
+        return T * 4 * K, T * 4 * K
+    raise ValueError(kernel)
 
 
 def scatter_kernel(w) -> str:
@@ -650,18 +666,70 @@ def layers_measure(benches, steps: int, warmup: int, check: bool, step_bytes: in
                 f"MISMATCH in layer {bad[0][0]}: {', '.join(bad[0][1])}")}
 
 
-def device_copy_gbps(torch, dev) -> float:
-    a = torch.empty(FLUSH_BYTES // 2, dtype=torch.int16, device=dev)
+PROBE_BYTES = 4 << 30  # 16x the 256 MB last-level cache: the probes see HBM, not the cache
+
+
+def hbm_rates(torch, dev, reps: int = 5, launches: int = 4) -> dict:
+    """HBM read, write and 1:1 copy rates from the streaming probe kernels
+    (libepdc_probe.so) over 4 GiB buffers: the median over `reps` event
+    pairs, each around `launches` back-to-back launches."""
+    from combine_routing_histogram_amd import probe
+
+    a = torch.zeros(PROBE_BYTES, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(10):
-        b.copy_(a)
-    c1.record()
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+
+    def rate(fn, moved: int) -> float:
+        fn()
+        times = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(launches):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / launches)
+        return moved / (statistics.median(times) * 1e-3) / 1e9
+
+    # `a` is all zeros, so its words never XOR to the magic 1
+    read = rate(lambda: probe.read(a.data_ptr(), PROBE_BYTES, 1, flag.data_ptr(), st),
+                PROBE_BYTES)
+    write = rate(lambda: probe.write(b.data_ptr(), PROBE_BYTES, 0, st), PROBE_BYTES)
+    copy = rate(lambda: probe.copy(a.data_ptr(), b.data_ptr(), PROBE_BYTES, st),
+                2 * PROBE_BYTES)
     torch.cuda.synchronize()
-    return 2 * FLUSH_BYTES / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+    assert int(flag.item()) == 0
+    del a, b
+    torch.cuda.empty_cache()
+    return {"read_gbps": read, "write_gbps": write, "copy_gbps": copy,
+            "buffer_bytes": PROBE_BYTES, "reps": reps, "launches_per_rep": launches}
+
+
+def kernel_ceilings(rates: dict, w, states: dict) -> dict:
+    """Each route, scatter and combine kernel's bytes priced at the probes'
+    rates: bound_us = read bytes / read rate + written bytes / write rate
+    (the two directions taken one after the other, so a kernel whose reads
+    and writes overlap without interfering could beat it), and
+    frac = bound_us / the kernel's mean event time in each cache state."""
+    out = {}
+    names = set()
+    for ks in states.values():
+        names.update(ks or {})
+    for k in sorted(names):
+        try:
+            r, wr = alg_read_write(k, w)
+        except ValueError:
+            continue
+        bound = r / rates["read_gbps"] / 1e3 + wr / rates["write_gbps"] / 1e3
+        rec = {"read_bytes": r, "write_bytes": wr, "bound_us": bound}
+        for state, ks in states.items():
+            if ks and k in ks:
+                rec[f"frac_{state}"] = bound / ks[k]["avg_us"]
+        out[k] = rec
+    return out
 
 
 def main() -> int:
@@ -709,8 +777,10 @@ def main() -> int:
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size "
                          "kernel for scaling rocprofv3 byte counters)")
-    ap.add_argument("--device-copy", type=int, default=1,
-                    help="also time a plain 512 MiB torch device copy for reference (0 = skip)")
+    ap.add_argument("--ceilings", "--device-copy", dest="ceilings", type=int, default=1,
+                    help="also measure the HBM read, write and copy rates with the probe "
+                         "kernels and price each kernel at them (0 = skip; --device-copy is "
+                         "the older name)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -778,7 +848,10 @@ def main() -> int:
     if args.clean_steps > 0:
         clean = measure(b, args.clean_steps, args.warmup, "read", check, step_bytes)
         log(f"clean flush: {clean['ms_per_step'] * 1e3:.1f} us/step")
-    copy_gbps = device_copy_gbps(torch, dev) if args.device_copy else None
+    rates = hbm_rates(torch, dev) if args.ceilings else None
+    if rates:
+        log(f"HBM probes: read {rates['read_gbps']:.0f} GB/s, write {rates['write_gbps']:.0f} "
+            f"GB/s, copy {rates['copy_gbps']:.0f} GB/s")
 
     # roofline: the kernel with the most time under the headline protocol
     roof = None
@@ -845,6 +918,8 @@ def main() -> int:
             if args.kernel_steps > 0:
                 r["kernels"] = kernel_table(eb.kernel_pass(args.kernel_steps, args.flush),
                                             ew, None)
+                if rates:
+                    r["ceilings"] = kernel_ceilings(rates, ew, {"headline": r["kernels"]})
             # the same workload in the two other cache states (step figures only)
             if args.clean_steps > 0:
                 r["clean_flush"] = measure(eb, args.clean_steps, args.warmup, "read", check, sb)
@@ -910,9 +985,10 @@ def main() -> int:
         "warm": warm,
         "layers": layers,
         "clean_flush": clean,
-        "device_copy": None if copy_gbps is None else {
-            "kernel": "512 MiB device-to-device copy (torch copy_), for reference",
-            "gbps": copy_gbps},
+        "ceilings": None if rates is None else dict(
+            rates, kernels=kernel_ceilings(rates, w, {
+                "headline": kernels, "warm": (warm or {}).get("kernels")})
+            if args.path == "pair" and args.combine == "gather" else None),
         "workloads": extras,
         "cpu_baseline": cpu,
         "parity": head["parity"] if check else "skipped",

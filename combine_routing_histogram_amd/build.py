@@ -1,4 +1,6 @@
-"""Build the gfx950 HIP library libepdc.so in place with hipcc.
+"""Build the gfx950 HIP libraries in place with hipcc: libepdc.so (the
+dispatch/combine path) and libepdc_probe.so (the HBM rate probes the
+benchmark compares it with).
 
 Flags: -O3 without fast-math (IEEE fp32 division, denormals kept), and the
 packed-fp32 instructions disabled for device code: hipcc would otherwise form
@@ -16,23 +18,26 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "epdc.hip")
 DEPS = [SRC, os.path.join(PKG, "csrc", "epdc_kernels.hpp"), os.path.join(ROOT, "include", "epdc.h")]
 LIB = os.path.join(PKG, "libepdc.so")
+PROBE_SRC = os.path.join(PKG, "csrc", "hbm_probe.hip")
+PROBE_DEPS = [PROBE_SRC, os.path.join(ROOT, "include", "epdc_probe.h"),
+              os.path.join(ROOT, "include", "epdc.h")]
+PROBE_LIB = os.path.join(PKG, "libepdc_probe.so")
 ARCH = "gfx950"
 
 
-def hipcc_command(out: str) -> list:
+def hipcc_command(out: str, src: str = SRC) -> list:
     return [
         "hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Wall", "-Wno-unused-command-line-argument",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", os.path.join(ROOT, "include"),
-        SRC, "-o", out,
+        src, "-o", out,
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile libepdc.so (always; a few seconds)."""
-    tmp = LIB + ".tmp"
-    cmd = hipcc_command(tmp)
+def _compile(src: str, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
+    cmd = hipcc_command(tmp, src)
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -43,7 +48,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msg}")
     if verbose and msg.strip():
         print(msg, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libepdc.so and libepdc_probe.so (always; a few seconds)."""
+    _compile(SRC, LIB, verbose)
+    _compile(PROBE_SRC, PROBE_LIB, verbose)
     _write_build_info()
     return LIB
 
@@ -68,10 +79,13 @@ def _write_build_info() -> None:
 
 
 def is_stale() -> bool:
-    if not os.path.exists(LIB):
-        return True
-    t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(d) > t for d in DEPS)
+    for lib, deps in ((LIB, DEPS), (PROBE_LIB, PROBE_DEPS)):
+        if not os.path.exists(lib):
+            return True
+        t = os.path.getmtime(lib)
+        if any(os.path.getmtime(d) > t for d in deps):
+            return True
+    return False
 
 
 if __name__ == "__main__":

@@ -64,3 +64,33 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_read_write_split_sums_to_the_algorithmic_bytes():
+    """The reads and writes the ceilings price add up to alg_bytes, and the
+    split follows the method: the scatter reads one row per token and writes
+    K, the combine the other way round."""
+    for w in wl.WORKLOADS.values():
+        T, H, K = w.tokens, w.hidden, w.topk
+        X, P, Q = bench.row_sizes(w)
+        for k in (bench.scatter_kernel(w), "k_combine", "k_route_rank"):
+            r, wr = bench.alg_read_write(k, w)
+            assert r + wr == bench.alg_bytes(k, w), (w.name, k)
+        r, wr = bench.alg_read_write(bench.scatter_kernel(w), w)
+        assert r == T * (X + 8 * K) and wr >= T * K * (P + Q)
+        r, wr = bench.alg_read_write("k_combine", w)
+        assert r >= T * K * 2 * H and wr == T * (2 * H + 4 * K)
+
+
+def test_kernel_ceilings_price_reads_and_writes():
+    w = wl.WORKLOADS["deepseek_v3_bf16"]
+    rates = {"read_gbps": 6000.0, "write_gbps": 5000.0}
+    states = {"headline": {"k_combine": {"avg_us": 100.0}, "k_check_indices": {"avg_us": 1.0}},
+              "warm": None}
+    c = bench.kernel_ceilings(rates, w, states)
+    assert set(c) == {"k_combine"}  # kernels with no read/write split are left out
+    r, wr = bench.alg_read_write("k_combine", w)
+    assert c["k_combine"]["bound_us"] == pytest.approx(r / 6e6 + wr / 5e6)  # bytes / (GB/s) in us
+    assert c["k_combine"]["frac_headline"] == pytest.approx(c["k_combine"]["bound_us"] / 100.0)
+    assert "frac_warm" not in c["k_combine"]
+

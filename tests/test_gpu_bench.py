@@ -45,9 +45,16 @@ def test_default_line():
     assert [leg["cores"] for leg in cpu["legs"]][0] == 1
     assert set(d["workloads"]) == {"deepseek_v3_fp8", "qwen3_moe_mxfp4", "decode_bf16",
                                    "deepseek_v3_raw_fp8"}
+    ce = d["ceilings"]
+    assert min(ce["read_gbps"], ce["write_gbps"], ce["copy_gbps"]) > 1000
+    assert max(ce["read_gbps"], ce["write_gbps"], ce["copy_gbps"]) < 8000
+    assert set(ce["kernels"]) >= {"k_scatter_copy", "k_combine"}
+    for k, v in ce["kernels"].items():
+        assert v["bound_us"] > 0 and v["frac_headline"] > 0 and v["frac_warm"] > 0, k
     for name, r in d["workloads"].items():
         assert r["parity"] == "bit-exact on all 3 timed steps", name
         assert r["ms_per_step"] > 0 and r["kernels"], name
+        assert r["ceilings"]["k_combine"]["bound_us"] > 0, name
         assert r["clean_flush"]["parity"] == "bit-exact on all 3 timed steps", name
         assert r["warm"]["parity"].startswith("bit-exact"), name
 
