@@ -708,12 +708,27 @@ def hbm_rates(torch, dev, reps: int = 5, launches: int = 4) -> dict:
             "buffer_bytes": PROBE_BYTES, "reps": reps, "launches_per_rep": launches}
 
 
+def mix_seconds_per_gb(read_frac: float, rates: dict) -> float:
+    """Time per GB of a stream whose fraction `read_frac` of the bytes are
+    reads, interpolated linearly between the probes' write-only (0), 1:1
+    copy (0.5) and read-only (1) rates."""
+    tw, tc, tr = (1 / rates["write_gbps"], 1 / rates["copy_gbps"], 1 / rates["read_gbps"])
+    if read_frac <= 0.5:
+        return tw + (tc - tw) * 2 * read_frac
+    return tc + (tr - tc) * (2 * read_frac - 1)
+
+
 def kernel_ceilings(rates: dict, w, states: dict) -> dict:
     """Each route, scatter and combine kernel's bytes priced at the probes'
-    rates: bound_us = read bytes / read rate + written bytes / write rate
-    (the two directions taken one after the other, so a kernel whose reads
-    and writes overlap without interfering could beat it), and
-    frac = bound_us / the kernel's mean event time in each cache state."""
+    rates, two ways:
+      bound_us     = read bytes / read rate + written bytes / write rate (the
+                     two directions one after the other with no interference
+                     between them: a floor no mixed stream reaches);
+      mix_bound_us = all bytes at the rate mix_seconds_per_gb gives for the
+                     kernel's read fraction (reads and writes interleaved as
+                     in the probes' copy);
+    and frac_<state> / frac_mix_<state> = bound / the kernel's mean event
+    time in each cache state."""
     out = {}
     names = set()
     for ks in states.values():
@@ -724,10 +739,12 @@ def kernel_ceilings(rates: dict, w, states: dict) -> dict:
         except ValueError:
             continue
         bound = r / rates["read_gbps"] / 1e3 + wr / rates["write_gbps"] / 1e3
-        rec = {"read_bytes": r, "write_bytes": wr, "bound_us": bound}
+        mix = (r + wr) * mix_seconds_per_gb(r / (r + wr), rates) / 1e3
+        rec = {"read_bytes": r, "write_bytes": wr, "bound_us": bound, "mix_bound_us": mix}
         for state, ks in states.items():
             if ks and k in ks:
                 rec[f"frac_{state}"] = bound / ks[k]["avg_us"]
+                rec[f"frac_mix_{state}"] = mix / ks[k]["avg_us"]
         out[k] = rec
     return out
 

@@ -84,7 +84,7 @@ def test_read_write_split_sums_to_the_algorithmic_bytes():
 
 def test_kernel_ceilings_price_reads_and_writes():
     w = wl.WORKLOADS["deepseek_v3_bf16"]
-    rates = {"read_gbps": 6000.0, "write_gbps": 5000.0}
+    rates = {"read_gbps": 6000.0, "write_gbps": 5000.0, "copy_gbps": 4000.0}
     states = {"headline": {"k_combine": {"avg_us": 100.0}, "k_check_indices": {"avg_us": 1.0}},
               "warm": None}
     c = bench.kernel_ceilings(rates, w, states)
@@ -93,4 +93,20 @@ def test_kernel_ceilings_price_reads_and_writes():
     assert c["k_combine"]["bound_us"] == pytest.approx(r / 6e6 + wr / 5e6)  # bytes / (GB/s) in us
     assert c["k_combine"]["frac_headline"] == pytest.approx(c["k_combine"]["bound_us"] / 100.0)
     assert "frac_warm" not in c["k_combine"]
+
+
+def test_mix_rate_interpolates_the_probes():
+    rates = {"read_gbps": 8000.0, "write_gbps": 4000.0, "copy_gbps": 2000.0}
+    assert bench.mix_seconds_per_gb(0.0, rates) == pytest.approx(1 / 4000)
+    assert bench.mix_seconds_per_gb(0.5, rates) == pytest.approx(1 / 2000)
+    assert bench.mix_seconds_per_gb(1.0, rates) == pytest.approx(1 / 8000)
+    assert bench.mix_seconds_per_gb(0.25, rates) == pytest.approx((1 / 4000 + 1 / 2000) / 2)
+    w = wl.WORKLOADS["deepseek_v3_bf16"]
+    c = bench.kernel_ceilings(rates, w, {"headline": {"k_scatter_copy": {"avg_us": 200.0}}})
+    r, wr = bench.alg_read_write("k_scatter_copy", w)
+    want = (r + wr) * bench.mix_seconds_per_gb(r / (r + wr), rates) / 1e3
+    assert c["k_scatter_copy"]["mix_bound_us"] == pytest.approx(want)
+    assert c["k_scatter_copy"]["frac_mix_headline"] == pytest.approx(want / 200.0)
+    # interleaving costs: the mixed bound is never below the one-after-the-other bound here
+    assert c["k_scatter_copy"]["mix_bound_us"] >= c["k_scatter_copy"]["bound_us"]
 

@@ -51,6 +51,7 @@ def test_default_line():
     assert set(ce["kernels"]) >= {"k_scatter_copy", "k_combine"}
     for k, v in ce["kernels"].items():
         assert v["bound_us"] > 0 and v["frac_headline"] > 0 and v["frac_warm"] > 0, k
+        assert v["mix_bound_us"] > 0 and v["frac_mix_headline"] > 0, k
     for name, r in d["workloads"].items():
         assert r["parity"] == "bit-exact on all 3 timed steps", name
         assert r["ms_per_step"] > 0 and r["kernels"], name
