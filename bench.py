@@ -884,6 +884,18 @@ def main() -> int:
             ph = head["combine"]["mean_us"]
             roof["achieved_timed_phase"] = dk["alg_bytes"] / (ph * 1e-6) / 1e9
 
+    ceilings = None
+    if rates is not None:
+        ceilings = dict(rates, kernels=None)
+        if args.path == "pair" and args.combine == "gather":
+            ceilings["kernels"] = kernel_ceilings(
+                rates, w, {"headline": kernels, "warm": (warm or {}).get("kernels")})
+            if roof and roof["kernel"] in ceilings["kernels"]:
+                c = ceilings["kernels"][roof["kernel"]]
+                # the same kernel against what this card's HBM delivers for its mix
+                roof["vs_measured_hbm"] = {k: c[k] for k in (
+                    "bound_us", "mix_bound_us", "frac_headline", "frac_mix_headline")}
+
     recent = b.recent
     b.op = None
     del b
@@ -1002,10 +1014,7 @@ def main() -> int:
         "warm": warm,
         "layers": layers,
         "clean_flush": clean,
-        "ceilings": None if rates is None else dict(
-            rates, kernels=kernel_ceilings(rates, w, {
-                "headline": kernels, "warm": (warm or {}).get("kernels")})
-            if args.path == "pair" and args.combine == "gather" else None),
+        "ceilings": ceilings,
         "workloads": extras,
         "cpu_baseline": cpu,
         "parity": head["parity"] if check else "skipped",

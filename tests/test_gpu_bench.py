@@ -39,6 +39,8 @@ def test_default_line():
     roof = d["roofline"]
     assert roof["bound"] == "hbm" and roof["peak"] == 8000.0 and roof["unit"] == "GB/s"
     assert 0 < roof["frac"] < 1 and abs(roof["achieved"] / roof["peak"] - roof["frac"]) < 1e-9
+    vs = roof["vs_measured_hbm"]
+    assert vs["bound_us"] > 0 and vs["frac_mix_headline"] > roof["frac"]
     assert set(d["kernels"]) >= {"k_route_rank", "k_scatter_copy", "k_combine"}
     cpu = d["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["openmp_result_identical"]
