@@ -7,7 +7,7 @@ per case, so tile and segment boundaries land in many different places.
 
 EPDC_SWEEP_CASES=N runs N seeds instead of 24; seeds from 24 on also draw,
 for about a third of the cases, 700-6000 tokens (many routing tiles, so the
-table is scanned by the last rank block).  All 424 seeds were run once.
+table is scanned by the last rank block).  Seeds 0-999 were run once.
 """
 import os
 
