@@ -32,6 +32,9 @@ def _host_sanitized(cmd):
 def sanitized(tmp_path_factory):
     if shutil.which("hipcc") is None:
         pytest.skip("no hipcc")
+    if os.environ.get("LD_PRELOAD"):
+        pytest.skip("the environment already preloads a library; the sanitizer runtime would "
+                    "have to take its place")
     rts = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
     if not rts:
         pytest.skip("no clang sanitizer runtime")

@@ -30,6 +30,9 @@ def _runtime(name):
 def sanitized(tmp_path_factory):
     if shutil.which("gcc") is None:
         pytest.skip("no gcc")
+    if os.environ.get("LD_PRELOAD"):
+        pytest.skip("the environment already preloads a library; the sanitizer runtime would "
+                    "have to take its place")
     asan, ubsan = _runtime("libasan.so"), _runtime("libubsan.so")
     if not asan or not ubsan:
         pytest.skip("gcc has no sanitizer runtimes here")
