@@ -5,9 +5,10 @@ dispatch with both conversions and the unit combine.  Shapes, payload kinds,
 routing skew, invalid ids, missing weights and ragged token counts are drawn
 per case, so tile and segment boundaries land in many different places.
 
-EPDC_SWEEP_CASES=N runs N seeds instead of 24; seeds from 24 on also draw,
-for about a third of the cases, 700-6000 tokens (many routing tiles, so the
-table is scanned by the last rank block).  Seeds 0-999 were run once.
+EPDC_SWEEP_CASES=N runs N seeds instead of 24, starting at EPDC_SWEEP_FIRST
+(default 0); seeds from 24 on also draw, for about a third of the cases,
+700-6000 tokens (many routing tiles, so the table is scanned by the last
+rank block).  Seeds 0-2499 were run once.
 """
 import os
 
@@ -67,9 +68,10 @@ def draw_case(rng):
 
 
 SWEEP_CASES = int(os.environ.get("EPDC_SWEEP_CASES", "24"))
+SWEEP_FIRST = int(os.environ.get("EPDC_SWEEP_FIRST", "0"))
 
 
-@pytest.mark.parametrize("seed", range(SWEEP_CASES))
+@pytest.mark.parametrize("seed", range(SWEEP_FIRST, SWEEP_FIRST + SWEEP_CASES))
 def test_random_configurations(seed):
     rng = np.random.default_rng(5000 + seed)
     c = draw_case(rng)
